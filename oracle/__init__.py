@@ -1,0 +1,6 @@
+"""CPU oracle for the Simple GLA mixer (float64, token by token).
+
+TEST INFRASTRUCTURE ONLY: used by the tests, the package smoke check and the
+benchmark's CPU-baseline leg.  The product path never imports it.
+"""
+from .gla_oracle import forward, step, backward, state_bytes  # noqa: F401

@@ -1,0 +1,137 @@
+"""Plain fp64 CPU oracle for the Simple GLA mixer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+run this module: only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP path.
+
+What it computes
+----------------
+The pages describe the mixer only in words ("Cómo i14 llevó Laplace 3B a AWS
+Trainium2", sections "Por qué atención lineal importa" and "Diseño esencial
+de Laplace 3B"; "AWS serve Laplace 3B di i14 con uno stato fisso di 29,5 MB",
+section "GLA sostituisce i token conservati con uno stato ricorrente"): every
+layer keeps a matrix state of fixed size, updates it once per token, lets it
+decay, and reads it by content with the query.  The plainest reading of that,
+with a scalar ("Simple") decay per head and token, is
+
+    S_t = gamma_t * S_{t-1} + k_t^T v_t          (S is dk x dv)
+    o_t = q_t S_t                                 (reads the updated state)
+    gamma_t = exp(g_t),  g_t <= 0 the log-decay
+
+with S_{-1} = S0 (zero when absent).  The pages give no scale on q, so there
+is none.  The chunk size (16 chunks of 128 tokens in the Trainium2 rewrite,
+section "Adaptaciones para AWS Trainium2", item 1) does not change the result
+and does not appear here: the oracle walks token by token.
+
+Everything is float64.  Inputs may be any float dtype; callers pass the exact
+values the device sees (bf16 inputs already rounded to bf16).
+
+Layouts: q, k [B, T, H, dk]; v, o, dO [B, T, H, dv]; g [B, T, H];
+S0, S_T, dS_T, dS0 [B, H, dk, dv].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["forward", "step", "backward", "state_bytes"]
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def forward(q, k, v, g, S0=None):
+    """Token-by-token recurrence.  Returns (o, S_T) in float64.
+
+    For each token t: gamma = exp(g_t) (exp(-inf) = 0 exactly), the state
+    decays, the outer product k_t^T v_t is added, and the query reads the
+    updated state.
+    """
+    q, k, v, g, S0 = _f64(q), _f64(k), _f64(v), _f64(g), _f64(S0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else S0.copy()
+    o = np.empty((B, T, H, dv))
+    for t in range(T):
+        gamma = np.exp(g[:, t, :])                       # [B, H]
+        S *= gamma[:, :, None, None]
+        S += k[:, t, :, :, None] * v[:, t, :, None, :]
+        o[:, t] = np.matmul(q[:, t, :, None, :], S)[:, :, 0, :]
+    return o, S
+
+
+def step(S, q, k, v, g):
+    """One decode step for a batch of sequences.
+
+    S [N, H, dk, dv]; q, k [N, H, dk]; v [N, H, dv]; g [N, H].
+    Returns (o [N, H, dv], S_new), both float64; S is not modified.
+    """
+    S = _f64(S).copy()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    S *= np.exp(g)[:, :, None, None]
+    S += k[:, :, :, None] * v[:, :, None, :]
+    o = np.matmul(q[:, :, None, :], S)[:, :, 0, :]
+    return o, S
+
+
+def backward(q, k, v, g, dO, S0=None, dS_T=None, ckpt=16):
+    """Reverse-mode gradient of L = <dO, o> + <dS_T, S_T> for `forward`.
+
+    Returns (dq, dk, dv, dg, dS0) in float64.  The pages state only that the
+    backward is sequential over the chunk steps ("Adaptaciones para AWS
+    Trainium2", item 3; "Trainium2 ha richiesto modifiche ai kernel e alla
+    comunicazione"); the steps below are the chain rule of the recurrence.
+
+    Let U_t be the gradient with respect to S_t through every later use.
+    Walking t from T-1 down to 0, with U starting at dS_T:
+        U   <- U + q_t^T dO_t          (the read-out of token t)
+        dq_t = S_t dO_t^T ; dk_t = U v_t^T ; dv_t = k_t U
+        dg_t = gamma_t * <U, S_{t-1}>  (d gamma / d g = gamma)
+        U   <- gamma_t U               (gradient reaching S_{t-1})
+    and dS0 = U at the end.  S_t is recomputed in float64 from checkpoints
+    taken every `ckpt` tokens, which reproduces the forward bit for bit.
+    """
+    q, k, v, g, dO = _f64(q), _f64(k), _f64(v), _f64(g), _f64(dO)
+    S0, dS_T = _f64(S0), _f64(dS_T)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else S0.copy()
+    gam = np.exp(g)                                       # [B, T, H]
+
+    # Forward pass keeping the state entering every block of `ckpt` tokens.
+    n_blk = (T + ckpt - 1) // ckpt
+    ck = np.empty((n_blk, B, H, dk, dv))
+    for t in range(T):
+        if t % ckpt == 0:
+            ck[t // ckpt] = S
+        S *= gam[:, t, :, None, None]
+        S += k[:, t, :, :, None] * v[:, t, :, None, :]
+
+    dq = np.empty_like(q)
+    dkk = np.empty_like(k)
+    dvv = np.empty_like(v)
+    dg = np.empty((B, T, H))
+    U = np.zeros((B, H, dk, dv)) if dS_T is None else dS_T.copy()
+    for blk in range(n_blk - 1, -1, -1):
+        t0, t1 = blk * ckpt, min(T, (blk + 1) * ckpt)
+        # states[i] = S_{t0 + i - 1}, i.e. states[0] is the state before t0.
+        states = np.empty((t1 - t0 + 1, B, H, dk, dv))
+        states[0] = ck[blk]
+        for t in range(t0, t1):
+            Sn = states[t - t0] * gam[:, t, :, None, None]
+            Sn += k[:, t, :, :, None] * v[:, t, :, None, :]
+            states[t - t0 + 1] = Sn
+        for t in range(t1 - 1, t0 - 1, -1):
+            S_t, S_prev = states[t - t0 + 1], states[t - t0]
+            U += q[:, t, :, :, None] * dO[:, t, :, None, :]
+            dq[:, t] = np.matmul(S_t, dO[:, t, :, :, None])[..., 0]
+            dkk[:, t] = np.matmul(U, v[:, t, :, :, None])[..., 0]
+            dvv[:, t] = np.matmul(k[:, t, :, None, :], U)[:, :, 0, :]
+            dg[:, t] = gam[:, t] * np.einsum("bhij,bhij->bh", U, S_prev)
+            U *= gam[:, t, :, None, None]
+    return dq, dkk, dvv, dg, U
+
+
+def state_bytes(H, dk, dv, itemsize=4):
+    """Bytes of one layer's recurrent state for one sequence (fp32 state)."""
+    return H * dk * dv * itemsize
