@@ -1,0 +1,181 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) Simple GLA mixer library (libgla.so).
+ *
+ * The mixer: every layer keeps a fixed-size matrix state per sequence and
+ * head, decays it once per token with a scalar gate and adds the token's
+ * key/value outer product; the query reads the updated state by content
+ * ("Cómo i14 llevó Laplace 3B a AWS Trainium2", sections "Por qué atención
+ * lineal importa" and "Diseño esencial de Laplace 3B"; "AWS serve Laplace 3B
+ * di i14 con uno stato fisso di 29,5 MB", section "GLA sostituisce i token
+ * conservati con uno stato ricorrente"):
+ *
+ *     S_t = exp(g_t) * S_{t-1} + k_t^T v_t ,   o_t = q_t S_t
+ *
+ * per (batch b, head h), S is dk x dv, S_{-1} = S0.  There is no scale on q
+ * (callers pre-scale).  Heads: H >= 1; dk = 96, dv = 192 and chunk = 128 are
+ * the sizes of the pages ("Diseño esencial de Laplace 3B"; "Adaptaciones para
+ * AWS Trainium2", item 1) and the only ones this library accepts.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers, dense row-major, in the layouts
+ *    given per argument; pointers must be 16-byte aligned.  The caller owns
+ *    every tensor and the workspace; the library never frees or keeps them.
+ *  - in_dtype (q, k, v, dO) and out_dtype (o, dq, dk, dv) are gla_dtype
+ *    values.  The log-decay g, states (S0, S_T, dS_T, dS0, pool) and dg are
+ *    always float32.  Accumulation and the carried state are float32.
+ *  - g <= 0 (or -inf for a state that forgets everything) is a caller
+ *    contract; g is clamped to GLA_G_MIN inside the kernels.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  They never synchronise and never allocate (except
+ *    gla_state_alloc).  Faults of running kernels surface at the caller's
+ *    next synchronisation.
+ *  - Arguments are validated before any HIP call.  A failing call returns a
+ *    non-zero gla_status, launches nothing, and leaves a message for
+ *    gla_last_error() in thread-local storage.  No exception crosses the ABI.
+ *  - Outputs must not alias inputs.  Calls on different streams that share
+ *    an output race.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, workspace too small */
+  GLA_ERR_UNSUPPORTED = 2,      /* a size or dtype this build does not implement */
+  GLA_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed (gla_state_alloc only) */
+  GLA_ERR_DEVICE = 4            /* the HIP runtime reported an error at launch */
+} gla_status;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+typedef enum { GLA_OP_FWD = 0, GLA_OP_BWD = 1 } gla_op;
+
+/* Lower clamp of the log-decay inside the kernels; exp(-60) ~ 8.8e-27. */
+#define GLA_G_MIN (-60.0f)
+
+/* Problem sizes of a prefill or backward call.  B, T, H >= 1; T need not be
+ * a multiple of `chunk` (the tail chunk is masked).  dk = 96, dv = 192,
+ * chunk = 128.  in_dtype/out_dtype are gla_dtype values. */
+typedef struct {
+  int64_t B, T;
+  int32_t H, dk, dv, chunk;
+  int32_t in_dtype, out_dtype;
+} gla_dims;
+
+/* Opaque pool of per-sequence recurrent states. */
+typedef struct gla_state gla_state;
+
+/* ---------------------------------------------------------------------------
+ * State pool.  The pages keep one fixed-size recurrent state per sequence in
+ * the serving engine's memory pool ("AWS serve Laplace 3B di i14 con uno stato
+ * fisso di 29,5 MB", section "Lo stato di Laplace 3B resta fisso durante
+ * l'inferenza"); its size does not depend on the context length, so the pool
+ * takes no T.
+ *
+ * gla_state_alloc: library-owned float32 pool [n_slots, H, dk, dv] on the
+ * current HIP device, 256-byte aligned, zero-filled in stream order on
+ * `stream` (a slot is H*dk*dv*4 bytes: 1,179,648 B at H=16).  n_slots >= 1.
+ * On success *out receives the handle; free it with gla_state_free.
+ * Errors: INVALID_ARGUMENT (null out, n_slots < 1, H < 1), UNSUPPORTED
+ * (dk != 96 or dv != 192), OUT_OF_MEMORY, DEVICE.
+ */
+gla_status gla_state_alloc(int64_t n_slots, int32_t H, int32_t dk, int32_t dv,
+                           void* stream, gla_state** out);
+
+/* Frees the pool (synchronises the device first so no kernel still uses it).
+ * NULL is accepted and ignored. */
+gla_status gla_state_free(gla_state* pool);
+
+/* Device pointer to slot `slot` ([H, dk, dv] float32), or NULL when the pool
+ * is NULL or the slot is out of range.  Prefill may read S0 from it and write
+ * S_T into it; a plain device copy saves or restores a slot. */
+float* gla_state_ptr(const gla_state* pool, int64_t slot);
+
+/* Number of slots of the pool (0 for NULL). */
+int64_t gla_state_slots(const gla_state* pool);
+
+/* Bytes of one slot: H*dk*dv*4. */
+size_t gla_state_slot_bytes(int32_t H, int32_t dk, int32_t dv);
+
+/* Workspace bytes that gla_chunk_fwd (op = GLA_OP_FWD) or gla_chunk_bwd
+ * (op = GLA_OP_BWD) needs for `dims`.  Same validation as those calls. */
+gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * Chunked prefill.  Computes o and the final state of the recurrence for T
+ * tokens, chunk by chunk: inside a chunk the decay-masked products of queries
+ * and keys weight the values, and the state carried between chunks adds the
+ * earlier context ("Adaptaciones para AWS Trainium2", item 1: 16 chunks of 128
+ * tokens; "Trainium2 ha richiesto modifiche ai kernel e alla comunicazione").
+ *
+ *   q, k : [B, T, H, dk]  in_dtype        v : [B, T, H, dv] in_dtype
+ *   g    : [B, T, H] float32 log-decay     S0: [B, H, dk, dv] float32 or NULL (zero)
+ *   o    : [B, T, H, dv] out_dtype        S_T: [B, H, dk, dv] float32 or NULL (not written)
+ *   ws   : device workspace of at least gla_workspace_size(GLA_OP_FWD) bytes
+ *          (may be NULL when that size is 0).
+ * S0 and S_T may point to the same memory (the initial state is read before
+ * the final state is written for each sequence).
+ */
+gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k,
+                         const void* v, const float* g, const float* S0, void* o,
+                         float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Batched single-token decode step, in place on a state pool.  For each of B
+ * sequences and each head: S <- exp(g) S + k^T v, then o = q S.  The state
+ * stays float32 and the cost per token does not depend on the context length
+ * ("I risultati dichiarati hanno limiti precisi": a longer prompt barely
+ * changes the cost per output token; "Resultados de entrenamiento e
+ * inferencia": 1,280 concurrent sequences).
+ *
+ *   q, k : [B, H, dk] in_dtype    v : [B, H, dv] in_dtype    g : [B, H] float32
+ *   pool : states; sequence b uses slot slot_idx[b] (device int32 [B]) or
+ *          slot b when slot_idx is NULL.  Indices must be in range and
+ *          distinct (caller contract, not checked on the device).
+ *   o    : [B, H, dv] out_dtype.
+ * Errors: INVALID_ARGUMENT (null pointers, B < 1, H or dk/dv differing from
+ * the pool's, B > slots when slot_idx is NULL), UNSUPPORTED, DEVICE.
+ */
+gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv,
+                              int32_t in_dtype, int32_t out_dtype, const void* q,
+                              const void* k, const void* v, const float* g,
+                              gla_state* pool, const int32_t* slot_idx, void* o,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Chunked backward.  Gradients of L = <dO, o> + <dS_T, S_T> with respect to
+ * q, k, v, the log-decay g and S0, computed chunk by chunk; the chunk steps
+ * are sequential in the reverse direction ("Adaptaciones para AWS Trainium2",
+ * item 3).  The forward states are recomputed; nothing from the forward call
+ * is needed.
+ *
+ *   q, k, v, g, S0 : as in gla_chunk_fwd (S0 NULL = zero)
+ *   dO   : [B, T, H, dv] in_dtype         dS_T : [B, H, dk, dv] float32 or NULL (zero)
+ *   dq, dk : [B, T, H, dk] out_dtype      dv : [B, T, H, dv] out_dtype
+ *   dg   : [B, T, H] float32              dS0 : [B, H, dk, dv] float32 or NULL (not written)
+ *   ws   : at least gla_workspace_size(GLA_OP_BWD) bytes.
+ * This build implements in_dtype = GLA_BF16 (UNSUPPORTED otherwise).
+ */
+gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k,
+                         const void* v, const float* g, const float* S0,
+                         const void* dO, const float* dS_T, void* dq, void* dk,
+                         void* dv, float* dg, float* dS0, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Errors. */
+const char* gla_status_str(gla_status status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* gla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GLA_H */

@@ -1,0 +1,273 @@
+"""Python binding of libgla, the gfx950 Simple GLA mixer library.
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, every step of the computation runs in the library's kernels.  The
+functions carry the names of the C entry points (include/gla.h):
+
+    gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None)        -> (o, S_T)
+    gla_recurrent_step(pool, q, k, v, g, slot_idx=None, out_dtype=None) -> o
+    gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None,
+                  want_dS0=False)                             -> (dq, dk, dv, dg, dS0)
+    gla_state_alloc(n_slots, H=16, dk=96, dv=192)             -> StatePool
+    gla_workspace_size(op, dims)                              -> int
+
+Layouts: q, k [B,T,H,96]; v, o, dO [B,T,H,192]; g [B,T,H] float32; states
+[B,H,96,192] float32.  There is no fallback: without the built library on a
+GPU every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDims",
+           "lib", "lib_path", "gla_chunk_fwd", "gla_recurrent_step", "gla_chunk_bwd",
+           "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS"]
+
+GLA_F32, GLA_BF16 = 0, 1
+GLA_OP_FWD, GLA_OP_BWD = 0, 1
+CHUNK, DK, DV = 128, 96, 192
+STATUS = {0: "GLA_OK", 1: "GLA_ERR_INVALID_ARGUMENT", 2: "GLA_ERR_UNSUPPORTED",
+          3: "GLA_ERR_OUT_OF_MEMORY", 4: "GLA_ERR_DEVICE"}
+EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slots",
+           "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
+           "gla_recurrent_step", "gla_chunk_bwd", "gla_status_str", "gla_last_error"]
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class GlaDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgla.so")
+
+
+def lib():
+    """Load libgla.so (built in-tree by build.py) and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m linear_attention_sequence_simple_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.gla_state_alloc.argtypes = [I64, I32, I32, I32, P, ctypes.POINTER(P)]
+    L.gla_state_free.argtypes = [P]
+    L.gla_state_ptr.argtypes = [P, I64]
+    L.gla_state_ptr.restype = P
+    L.gla_state_slots.argtypes = [P]
+    L.gla_state_slots.restype = I64
+    L.gla_state_slot_bytes.argtypes = [I32, I32, I32]
+    L.gla_state_slot_bytes.restype = SZ
+    L.gla_workspace_size.argtypes = [I32, ctypes.POINTER(GlaDims), ctypes.POINTER(SZ)]
+    L.gla_chunk_fwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, SZ, P]
+    L.gla_recurrent_step.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
+    L.gla_chunk_bwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.gla_status_str.argtypes = [I32]
+    L.gla_status_str.restype = ctypes.c_char_p
+    L.gla_last_error.restype = ctypes.c_char_p
+    for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd",
+                 "gla_recurrent_step", "gla_chunk_bwd"):
+        getattr(L, name).restype = I32
+    _LIB = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        raise GlaError(status, lib().gla_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GLA_F32
+    if t == torch.bfloat16:
+        return GLA_BF16
+    raise TypeError(f"unsupported dtype {t}: use torch.float32 or torch.bfloat16")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.float32 if code == GLA_F32 else torch.bfloat16
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(B, T, H, in_dtype, out_dtype) -> GlaDims:
+    return GlaDims(B, T, H, DK, DV, CHUNK, in_dtype, out_dtype)
+
+
+def gla_workspace_size(op: int, dims: GlaDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gla_workspace_size(op, ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} B < {nbytes} B")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspace=None, o=None,
+                  S_T=None):
+    """Chunked prefill.  Returns (o, S_T); S_T is None when want_state is False."""
+    B, T, H, _ = q.shape
+    dev = q.device
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    _need(q, "q", (B, T, H, DK), q.dtype, dev)
+    _need(k, "k", (B, T, H, DK), q.dtype, dev)
+    _need(v, "v", (B, T, H, DV), q.dtype, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, DK, DV), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, DV), dtype=_torch_dtype(out_code), device=dev)
+    _need(o, "o", (B, T, H, DV), _torch_dtype(out_code), dev)
+    if want_state and S_T is None:
+        S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need(S_T, "S_T", (B, H, DK, DV), torch.float32, dev)
+    dims = _dims(B, T, H, in_code, out_code)
+    ws = _workspace(gla_workspace_size(GLA_OP_FWD, dims), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gla_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
+                               _ptr(o), _ptr(S_T), _ptr(ws), nbytes, _stream()))
+    return o, S_T
+
+
+def gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None, want_dS0=False,
+                  workspace=None):
+    """Chunked backward.  Returns (dq, dk, dv, dg, dS0); dS0 is None unless want_dS0."""
+    B, T, H, _ = q.shape
+    dev = q.device
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    _need(q, "q", (B, T, H, DK), q.dtype, dev)
+    _need(k, "k", (B, T, H, DK), q.dtype, dev)
+    _need(v, "v", (B, T, H, DV), q.dtype, dev)
+    _need(dO, "dO", (B, T, H, DV), q.dtype, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _need(t, name, (B, H, DK, DV), torch.float32, dev)
+    od = _torch_dtype(out_code)
+    dq = torch.empty((B, T, H, DK), dtype=od, device=dev)
+    dk = torch.empty((B, T, H, DK), dtype=od, device=dev)
+    dv = torch.empty((B, T, H, DV), dtype=od, device=dev)
+    dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_dS0 else None
+    dims = _dims(B, T, H, in_code, out_code)
+    ws = _workspace(gla_workspace_size(GLA_OP_BWD, dims), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gla_chunk_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
+                               _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                               _ptr(dS0), _ptr(ws), nbytes, _stream()))
+    return dq, dk, dv, dg, dS0
+
+
+class StatePool:
+    """A library-owned float32 pool of recurrent states [n_slots, H, dk, dv]."""
+
+    def __init__(self, n_slots, H=16, dk=DK, dv=DV):
+        handle = ctypes.c_void_p()
+        _check(lib().gla_state_alloc(n_slots, H, dk, dv, _stream(), ctypes.byref(handle)))
+        self._h = handle
+        self.n_slots, self.H, self.dk, self.dv = n_slots, H, dk, dv
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("the pool has been freed")
+        return self._h
+
+    def ptr(self, slot=0) -> int:
+        p = lib().gla_state_ptr(self.handle, slot)
+        if not p:
+            raise IndexError(f"slot {slot} out of range [0, {self.n_slots})")
+        return p
+
+    @property
+    def slot_bytes(self) -> int:
+        return lib().gla_state_slot_bytes(self.H, self.dk, self.dv)
+
+    @property
+    def __cuda_array_interface__(self):
+        return {"shape": (self.n_slots, self.H, self.dk, self.dv), "typestr": "<f4",
+                "data": (self.ptr(0), False), "version": 3, "strides": None}
+
+    def view(self) -> torch.Tensor:
+        """A torch tensor aliasing the pool (no copy)."""
+        return torch.as_tensor(self, device=self.device)
+
+    def free(self):
+        if self._h is not None:
+            _check(lib().gla_state_free(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def gla_state_alloc(n_slots, H=16, dk=DK, dv=DV) -> StatePool:
+    return StatePool(n_slots, H, dk, dv)
+
+
+def gla_recurrent_step(pool: StatePool, q, k, v, g, slot_idx=None, out_dtype=None, o=None):
+    """One decode token per sequence; updates the pool in place and returns o [B,H,dv]."""
+    B, H, _ = q.shape
+    dev = q.device
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    _need(q, "q", (B, H, DK), q.dtype, dev)
+    _need(k, "k", (B, H, DK), q.dtype, dev)
+    _need(v, "v", (B, H, DV), q.dtype, dev)
+    _need(g, "g", (B, H), torch.float32, dev)
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", (B,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((B, H, DV), dtype=_torch_dtype(out_code), device=dev)
+    _need(o, "o", (B, H, DV), _torch_dtype(out_code), dev)
+    _check(lib().gla_recurrent_step(B, H, DK, DV, in_code, out_code, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(g), pool.handle, _ptr(slot_idx), _ptr(o), _stream()))
+    return o

@@ -1,0 +1,49 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+import numpy as np
+import torch
+
+import gen
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def to_dev(x, dtype):
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev()).to(dtype)
+
+
+def to_np(t):
+    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    """max |got - ref| / rms(ref), in float64."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(got - ref)) / rms) if rms > 0 else float(np.max(np.abs(got - ref)))
+
+
+def assert_close(got, ref, tol, name):
+    e = rel_err(got, ref)
+    print(f"  {name}: max|err|/rms = {e:.3e} (tol {tol:.0e})", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: max|err|/rms(ref) = {e:.3e} > {tol:.1e}"
+    return e
+
+
+def assert_close_bf16_out(got, ref, tol, name):
+    """bf16 outputs: |got - ref| <= tol*rms(ref) + 2^-8 |ref| elementwise."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    bound = tol * rms + 2.0 ** -8 * np.abs(ref)
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{name}: {bad.sum()} elements outside the bf16-output bound"
+
+
+def inputs(workload, seed=0, **kw):
+    return gen.make_inputs(workload, seed=seed, **kw)

@@ -1,0 +1,101 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, and rejects bad arguments before any HIP call (no device needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_simple_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gla.lib_path()):
+        pytest.skip("libgla.so not built")
+    return gla.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(gla.EXPORTS), names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def dims(**kw):
+    d = dict(B=2, T=300, H=16, dk=96, dv=192, chunk=128, in_dtype=gla.GLA_BF16, out_dtype=gla.GLA_F32)
+    d.update(kw)
+    return gla.GlaDims(**d)
+
+
+def ws_size(L, op, d):
+    n = ctypes.c_size_t(123)
+    st = L.gla_workspace_size(op, ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_status_strings(L):
+    for code, name in gla.STATUS.items():
+        assert L.gla_status_str(code).decode() == name
+
+
+def test_workspace_sizes(L):
+    st, n = ws_size(L, gla.GLA_OP_FWD, dims())
+    assert st == 0
+    st, n = ws_size(L, gla.GLA_OP_BWD, dims())
+    assert st == 0
+    # three bf16 copies of every chunk's state (states, two gradient layouts)
+    n_chunks = 3
+    assert n >= 3 * 2 * 16 * n_chunks * 96 * 192 * 2
+    st, _ = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32))
+    assert st == 2 and "bf16" in L.gla_last_error().decode()
+    st, _ = ws_size(L, 7, dims())
+    assert st == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(T=0), 1), (dict(H=0), 1), (dict(dk=64), 2), (dict(dv=128), 2),
+    (dict(chunk=64), 2), (dict(in_dtype=5), 1), (dict(out_dtype=-1), 1)])
+def test_dims_validation(L, kw, status):
+    st, _ = ws_size(L, gla.GLA_OP_FWD, dims(**kw))
+    assert st == status
+    assert L.gla_last_error().decode() != ""
+
+
+def test_pointer_validation(L):
+    d = dims()
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    bad = ctypes.c_void_p(0x10004)       # misaligned
+    st = L.gla_chunk_fwd(ctypes.byref(d), None, p, p, p, None, p, None, None, 0, None)
+    assert st == 1 and "q must not be NULL" in L.gla_last_error().decode()
+    st = L.gla_chunk_fwd(ctypes.byref(d), p, bad, p, p, None, p, None, None, 0, None)
+    assert st == 1 and "aligned" in L.gla_last_error().decode()
+    st = L.gla_chunk_bwd(ctypes.byref(d), p, p, p, p, None, p, None, p, p, p, None, None, p, 10, None)
+    assert st == 1 and "dg" in L.gla_last_error().decode()
+    _, need = ws_size(L, gla.GLA_OP_BWD, d)
+    st = L.gla_chunk_bwd(ctypes.byref(d), p, p, p, p, None, p, None, p, p, p, p, None, p, need - 1, None)
+    assert st == 1 and "workspace too small" in L.gla_last_error().decode()
+    st = L.gla_recurrent_step(4, 16, 96, 192, 1, 1, p, p, p, p, None, None, p, None)
+    assert st == 1 and "pool" in L.gla_last_error().decode()
+    st = L.gla_recurrent_step(0, 16, 96, 192, 1, 1, p, p, p, p, None, None, p, None)
+    assert st == 1
+
+
+def test_state_pool_validation(L):
+    h = ctypes.c_void_p()
+    assert L.gla_state_alloc(0, 16, 96, 192, None, ctypes.byref(h)) == 1
+    assert L.gla_state_alloc(4, 16, 64, 192, None, ctypes.byref(h)) == 2
+    assert L.gla_state_alloc(4, 16, 96, 192, None, None) == 1
+    assert L.gla_state_ptr(None, 0) is None
+    assert L.gla_state_slots(None) == 0
+    assert L.gla_state_slot_bytes(16, 96, 192) == 1_179_648
+    assert L.gla_state_free(None) == 0
