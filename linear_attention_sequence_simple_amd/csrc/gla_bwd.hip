@@ -106,8 +106,8 @@ __device__ __forceinline__ void bwd_wave(const BwdArgs& a, BwdSmem& sm, int64_t 
       for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 bk = frag_kcP(sm.k, PX, 32 * W, 32 * kb, s);
-          const int f = (cb * 3 + kb) * 2 + s;
+          const bf16x8 bk = frag_kcN(sm.k, PX, 32 * W, 32 * kb, s);
+          const int f = cb * 6 + kb * 2 + s;
           acc = mfma(gfrag(dScd, f), bk, acc);
           acc = mfma(gfrag(dScd + DK * DV, f), bk, acc);
         }

@@ -54,9 +54,14 @@ template <class T> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; static constexpr int SUB = 2; };
 template <> struct Frag<float> { typedef float type; static constexpr int SUB = 16; };
 
-__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+typedef const LDS_AS bf16* lds_cptr;
+// A generic pointer into shared memory as an LDS-address-space pointer, so
+// that constant offsets fold into the DS instructions' offset field.
+__device__ __forceinline__ lds_cptr to_lds(const bf16* p) { return (lds_cptr)(p); }
+__device__ __forceinline__ bf16x4 lds_tr4(lds_cptr p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p));
 }
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) { return lds_tr4(to_lds(p)); }
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -77,6 +82,13 @@ __device__ __forceinline__ float frag_kr(const float* M, int pitch, int row0, in
   return M[(row0 + 8 * (s >> 2) + 4 * g + (s & 3)) * pitch + col0 + (l & 31)];
 }
 
+// As frag_kr, in the plain contraction order (k = 16s + 8g + e).
+__device__ __forceinline__ bf16x8 frag_krN(const bf16* M, int pitch, int row0, int col0, int s) {
+  const int l = lane_id(), G = l >> 4, g = G >> 1, h = G & 1, L = l & 15;
+  const bf16* p = M + (row0 + 16 * s + 8 * g + (L >> 2)) * pitch + col0 + 16 * h + 4 * (L & 3);
+  return cat(lds_tr4(p), lds_tr4(p + 4 * pitch));
+}
+
 __device__ __forceinline__ bf16x8 frag_kcP(const bf16* M, int pitch, int row0, int col0, int s) {
   const int l = lane_id(), g = l >> 5;
   const bf16* p = M + (row0 + (l & 31)) * pitch + col0 + 16 * s + 4 * g;
@@ -93,6 +105,48 @@ __device__ __forceinline__ bf16x8 frag_kcN(const bf16* M, int pitch, int row0, i
 }
 __device__ __forceinline__ float frag_kcN(const float* M, int pitch, int row0, int col0, int s) {
   return frag_kcP(M, pitch, row0, col0, s);
+}
+
+// --- bf16 tiles [rows][96] without padding, 16-byte units XOR-swizzled by
+// (row >> 2) & 3.  With 64 banks of 4 bytes this makes the transposed reads
+// (4 rows x 64 bytes per 32 lanes) and the row reads (16 rows x 16 bytes per
+// 16 lanes) free of bank conflicts.
+__device__ __forceinline__ int swz96(int row, int col) {
+  return row * 96 + ((((col >> 3) ^ ((row >> 2) & 3))) << 3) + (col & 7);
+}
+// Hot-loop loaders for row0, col0 multiples of 32: the swizzle key then
+// depends on the lane only, so each access is a per-lane offset (computed once)
+// plus a compile-time offset.
+__device__ __forceinline__ bf16x8 sfrag_kr(const bf16* M, int row0, int col0, int s) {
+  const int l = lane_id(), g = l >> 5, h = (l >> 4) & 1, L = l & 15;
+  const int rowl = 4 * g + (L >> 2), ul = 2 * h + ((L & 3) >> 1), hl = 4 * (L & 1);
+  const int off1 = rowl * 96 + ((ul ^ g) << 3) + hl;
+  const int off2 = (rowl + 8) * 96 + ((ul ^ (g + 2)) << 3) + hl;
+  const lds_cptr base = to_lds(M) + (row0 + 16 * s) * 96 + col0;
+  return cat(lds_tr4(base + off1), lds_tr4(base + off2));
+}
+__device__ __forceinline__ bf16x8 sfrag_krN(const bf16* M, int row0, int col0, int s) {
+  const int l = lane_id(), g = l >> 5, h = (l >> 4) & 1, L = l & 15;
+  const int rowl = 8 * g + (L >> 2), ul = 2 * h + ((L & 3) >> 1), hl = 4 * (L & 1);
+  const int off1 = rowl * 96 + ((ul ^ (2 * g)) << 3) + hl;
+  const int off2 = (rowl + 4) * 96 + ((ul ^ (2 * g + 1)) << 3) + hl;
+  const lds_cptr base = to_lds(M) + (row0 + 16 * s) * 96 + col0;
+  return cat(lds_tr4(base + off1), lds_tr4(base + off2));
+}
+__device__ __forceinline__ bf16x8 sfrag_kcN(const bf16* M, int row0, int col0, int s) {
+  const int l = lane_id(), g = l >> 5, r = l & 31, key = (r >> 2) & 3;
+  const int off = r * 96 + (((2 * s + g) ^ key) << 3);
+  return *(const LDS_AS bf16x8*)(to_lds(M) + row0 * 96 + col0 + off);
+}
+// General (any row0, col0) versions for cold paths.
+__device__ __forceinline__ bf16x8 sfrag_kcN_any(const bf16* M, int row0, int col0, int s) {
+  const int l = lane_id(), g = l >> 5;
+  return *(const bf16x8*)(M + swz96(row0 + (l & 31), col0 + 16 * s + 8 * g));
+}
+__device__ __forceinline__ bf16x8 sfrag_krN_any(const bf16* M, int row0, int col0, int s) {
+  const int l = lane_id(), G = l >> 4, g = G >> 1, h = G & 1, L = l & 15;
+  const int r = row0 + 16 * s + 8 * g + (L >> 2), c = col0 + 16 * h + 4 * (L & 3);
+  return cat(lds_tr4(M + swz96(r, c)), lds_tr4(M + swz96(r + 4, c)));
 }
 
 // Contraction row (within a 32-block) of register/element e of sub-step s.
@@ -120,6 +174,39 @@ __device__ __forceinline__ bf16x8 scale_k(bf16x8 a, const float* w, int s) {
 }
 __device__ __forceinline__ float scale_k(float a, const float* w, int s) {
   return a * w[kidx_f32(s)];
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair (round to nearest even, one instruction).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo_f(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
+
+// hi = bf16(x), lo = bf16(x - hi) for a pair of floats.
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(a, b);
+  lo = pk_bf16(a - bf16_lo_f(hi), b - bf16_hi_f(hi));
+}
+
+// Split 8 floats (as 4 pairs) into compensated bf16x8 hi/lo operands.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split_pk(x[2 * i], x[2 * i + 1], h[i], l[i]);
+  hi = __builtin_bit_cast(bf16x8, *(uint4*)h);
+  lo = __builtin_bit_cast(bf16x8, *(uint4*)l);
+}
+
+// The compensated operand pair for sub-step s of a result tile's registers.
+__device__ __forceinline__ void split_tile(const f32x16& t, int s, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split_pk(t[8 * s + 2 * i], t[8 * s + 2 * i + 1], h[i], l[i]);
+  hi = __builtin_bit_cast(bf16x8, *(uint4*)h);
+  lo = __builtin_bit_cast(bf16x8, *(uint4*)l);
 }
 
 // Error-compensated bf16 operands: x ~= hi + lo with hi = bf16(x) and

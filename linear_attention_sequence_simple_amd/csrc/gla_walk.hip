@@ -1,7 +1,7 @@
 // Chunk walk kernels of the Simple GLA mixer for gfx950.
 //
-// One workgroup (4 waves) walks the chunks of one (batch, head, dv-slice,
-// segment) in order, keeping the recurrent state in matrix-core accumulators.
+// One workgroup walks the chunks of one (batch, head, dv-slice, segment) in
+// order, keeping the recurrent state in matrix-core accumulators.
 // Chunk formulation (chunks of 128 tokens, "Adaptaciones para AWS Trainium2",
 // item 1, of the page "Cómo i14 llevó Laplace 3B a AWS Trainium2"): with b_i
 // the running sum of the log-decay inside the chunk, Lambda_i = e^{b_i},
@@ -14,8 +14,11 @@
 // with the same code (X = Q, Y = dO, weights Lambda, chunks in reverse).
 //
 // The state is held transposed, Z^T[c][d], as 32x32 tiles (c rows, d cols)
-// spread over the 4 waves.  Wave w owns the output rows (tokens) 32w..32w+31
-// of each chunk.
+// spread over the "state" waves.  The prefill with output runs 8 waves, two
+// per SIMD: output wave w (0..3) owns the tokens 32w..32w+31 of each chunk
+// (scores, state read-out, P V) and state wave 4+u updates a share of the
+// state tiles; the shares are uneven so that each SIMD's pair of waves has
+// about the same matrix-core work.  The state-only walks run 4 state waves.
 //
 // With bf16 inputs the inputs themselves are exact MFMA operands, but the
 // intermediates (decay-masked scores, the bf16 copy of the fp32 state, the
@@ -27,25 +30,31 @@
 
 namespace gla {
 
+template <int MODE>
+struct WalkShape {
+  static constexpr bool OUT = MODE == WALK_FWD_OUT;
+  static constexpr int WAVES = OUT ? 8 : 4;
+  static constexpr int THREADS = 64 * WAVES;
+};
+
 template <int NC, bool OUT>
 struct Own {
-  // Z tiles t = cb*3 + db, contiguous ranges per wave.  With the output on,
-  // waves with fewer causal score tiles take more state tiles.
-  static constexpr int count(int w) {
+  // State tiles t = cb*3 + db owned by state wave u, contiguous ranges.  With
+  // the output on, state wave u shares a SIMD with output wave u, whose work
+  // grows with u.
+  static constexpr int count(int u) {
     if (OUT) {
-      if (NC == 3) return w == 0 ? 5 : w == 1 ? 3 : w == 2 ? 1 : 0;
-      if (NC == 2) return w == 0 ? 3 : w == 1 ? 2 : w == 2 ? 1 : 0;
-      if (NC == 1) return w == 0 ? 2 : w == 1 ? 1 : 0;
+      if (NC == 3) return u == 0 ? 4 : u == 1 ? 3 : u == 2 ? 2 : 0;
+      if (NC == 2) return u == 0 ? 3 : u == 1 ? 2 : u == 2 ? 1 : 0;
     } else {
-      if (NC == 3) return w == 0 ? 3 : 2;
-      if (NC == 2) return w < 2 ? 2 : 1;
-      if (NC == 1) return w < 3 ? 1 : 0;
+      if (NC == 3) return u == 0 ? 3 : 2;
+      if (NC == 2) return u < 2 ? 2 : 1;
     }
     return 0;
   }
-  static constexpr int first(int w) {
+  static constexpr int first(int u) {
     int f = 0;
-    for (int i = 0; i < w; ++i) f += count(i);
+    for (int i = 0; i < u; ++i) f += count(i);
     return f;
   }
   static_assert(first(4) == 3 * NC, "every state tile needs an owner");
@@ -56,31 +65,62 @@ template <> struct Pad<float> { static constexpr int v = 4; };
 
 template <class TIn, int NC, bool OUT>
 struct WalkSmem {
+  static constexpr bool COMP = sizeof(TIn) == 2;   // bf16 inputs: compensated intermediates
   static constexpr int DVS = 32 * NC;
-  static constexpr int PX = DK + Pad<TIn>::v;
-  static constexpr int PY = DVS + (sizeof(TIn) == 2 ? 8 : 0);
-  static constexpr int PZ = DVS + (sizeof(TIn) == 2 ? 8 : 0);
-  TIn x[CH * PX];
-  TIn y[CH * PY];
-  TIn q[OUT ? CH * PX : 16];
-  TIn z[DK * PZ];
-  TIn zl[sizeof(TIn) == 2 ? DK * PZ : 16];   // residual of the bf16 state copy
-  DecayLds dec;
+  // bf16 tiles use the swizzled unpadded [rows][96] layout (swz96); fp32
+  // tiles are padded row-major.
+  static_assert(!COMP || DVS == 96, "the swizzled bf16 layout assumes 96 columns");
+  static constexpr int PX = COMP ? DK : DK + Pad<TIn>::v;
+  static constexpr int PY = DVS;
+  static constexpr int PZ = DVS;
+  static constexpr int PQ = DK;                    // fp32 queries: unpadded (LDS budget)
+  TIn x[CH * PX];                         // keys (reverse walk: queries), as loaded
+  TIn xh[COMP ? CH * PX : 8];             // decay-weighted keys: bf16 value ...
+  TIn xl[COMP ? CH * PX : 8];             // ... and bf16 residual
+  TIn y[CH * PY];                         // values (reverse walk: dO), this dv-slice
+  TIn q[(OUT && !COMP) ? CH * PQ : 8];    // queries (fp32 inputs only; bf16 queries stay in registers)
+  TIn z[DK * PZ];                         // state entering the chunk, [d][c]
+  TIn zl[COMP ? DK * PZ : 8];             // residual of its bf16 copy
+  // Decay tables of the chunk being processed and of the next one (built a
+  // chunk ahead so the weighted keys can be written before the main barrier).
+  DecayLds dec[2];
+  // utab[U(I) + j] = 2^{b_{32I} - b_j} for j < 32I (I = 1, 2, 3; U = 0, 32, 96):
+  // the key-side factor of the decay between token blocks.
+  float utab[2][OUT ? 192 : 4];
 };
+
+__device__ __forceinline__ int utab_off(int I) { return I == 1 ? 0 : I == 2 ? 32 : 96; }
+
+// Block-boundary decay factors, by the wave that built the decay tables (its
+// lanes hold b of tokens 2l, 2l+1).
+__device__ __forceinline__ void build_utab(float* utab, const DecayLds* d) {
+  const int l = lane_id();
+#pragma unroll
+  for (int I = 1; I < 4; ++I) {
+    const float bref = d->b2[32 * I];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * l + e;
+      if (j < 32 * I) utab[utab_off(I) + j] = exp2f(bref - d->b2[j]);
+    }
+  }
+}
 
 // Rows [t0, t0+128) of a [B,T,H,D] tensor, columns [col0, col0+W), as 16-byte
 // pieces held in registers; rows past T read as zero.
-template <class T, int WCOLS>
+template <class T, int WCOLS, int NTHR>
 struct TileRegs {
+  // loader threads are numbered 0..NTHR-1 (the state waves of the workgroup)
   static constexpr int EPP = 16 / sizeof(T);           // elements per piece
   static constexpr int PPR = WCOLS / EPP;              // pieces per row
   static constexpr int NP = CH * PPR;
-  static constexpr int PER = (NP + 255) / 256;
+  static constexpr int PER = (NP + NTHR - 1) / NTHR;
   uint4 r[PER];
   __device__ __forceinline__ void load(const T* base, int64_t row_stride, int t0, int64_t T_len) {
+    const int tid = threadIdx.x & (NTHR - 1);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int p = threadIdx.x + 256 * i;
+      const int p = tid + NTHR * i;
       const int row = p / PPR, cp = p % PPR;
       if (p < NP && t0 + row < T_len)
         r[i] = *(const uint4*)(base + (int64_t)(t0 + row) * row_stride + cp * EPP);
@@ -90,12 +130,38 @@ struct TileRegs {
   }
   template <int PITCH>
   __device__ __forceinline__ void store(T* lds) const {
+    const int tid = threadIdx.x & (NTHR - 1);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int p = threadIdx.x + 256 * i;
+      const int p = tid + NTHR * i;
       if (p < NP) {
         const int row = p / PPR, cp = p % PPR;
-        *(uint4*)(lds + row * PITCH + cp * EPP) = r[i];
+        const int off = (sizeof(T) == 2) ? swz96(row, cp * EPP) : row * PITCH + cp * EPP;
+        *(uint4*)(lds + off) = r[i];
+      }
+    }
+  }
+  // bf16 rows scaled by w[row], stored as compensated hi/lo copies.
+  template <int PITCH>
+  __device__ __forceinline__ void store_weighted(bf16* hi, bf16* lo, const float* w) const {
+    const int tid = threadIdx.x & (NTHR - 1);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = tid + NTHR * i;
+      if (p < NP) {
+        const int row = p / PPR, cp = p % PPR;
+        const float s = w[row];
+        const uint32_t u[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+        float f[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[2 * k] = bf16_lo_f(u[k]) * s;
+          f[2 * k + 1] = bf16_hi_f(u[k]) * s;
+        }
+        bf16x8 h8, l8;
+        split8(f, h8, l8);
+        *(bf16x8*)(hi + swz96(row, cp * EPP)) = h8;
+        *(bf16x8*)(lo + swz96(row, cp * EPP)) = l8;
       }
     }
   }
@@ -109,10 +175,14 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   using S = WalkSmem<TIn, NC, OUT>;
   using FT = typename Frag<TIn>::type;
   constexpr int SUB = Frag<TIn>::SUB;
-  constexpr int NT = Own<NC, OUT>::count(W);
-  constexpr int T0 = Own<NC, OUT>::first(W);
+  constexpr bool OUTW = OUT && W < 4;                // output wave (else: state wave)
+  constexpr int U = OUT ? W - 4 : W;                  // index among the state waves
+  constexpr int NT = OUTW ? 0 : Own<NC, OUT>::count(U);
+  constexpr int T0 = OUTW ? 0 : Own<NC, OUT>::first(U);
   constexpr int DVS = 32 * NC;
-  constexpr bool COMP = sizeof(TIn) == 2;
+  constexpr bool COMP = S::COMP;
+  constexpr int NTHR = 256;                           // loader threads: the 4 state waves
+  constexpr bool LOADER = !OUTW;
 
   const int lane = lane_id();
   const int g2 = lane >> 5;
@@ -129,7 +199,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   const int n_end = min(a.n_chunks, n_begin + a.cps);
   const int nloc = n_end - n_begin;
 
-  // ---- state tiles: load the initial state or start from zero
+  // ---- state tiles Z^T (c rows, d columns): initial state or zero
   f32x16 z[NT > 0 ? NT : 1];
   {
     const float* zi = a.zinit ? a.zinit + bh * a.zinit_bh_stride + (int64_t)gseg * a.zinit_seg_stride : nullptr;
@@ -146,33 +216,74 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     }
   }
 
-  TileRegs<TIn, DK> px;
-  TileRegs<TIn, DVS> py;
-  TileRegs<TIn, OUT ? DK : 8> pq;
-  float gx0 = 0.f, gx1 = 0.f;
+  TileRegs<TIn, DK, NTHR> px;
+  TileRegs<TIn, DVS, NTHR> py;
+  TileRegs<TIn, (OUT && !COMP) ? DK : 8, NTHR> pq;
+  // bf16 queries of this output wave's 32 tokens, as plain-order MFMA B operands
+  bf16x8 qcur[(OUTW && COMP) ? 3 : 1][2], qnxt[(OUTW && COMP) ? 3 : 1][2];
   auto prefetch = [&](int n) {
     const int t0 = n * CH;
-    px.load(Xb, (int64_t)a.H * DK, t0, T);
-    py.load(Yb, (int64_t)a.H * DV, t0, T);
-    if constexpr (OUT) pq.load(Qb, (int64_t)a.H * DK, t0, T);
+    if constexpr (LOADER) {
+      px.load(Xb, (int64_t)a.H * DK, t0, T);
+      py.load(Yb, (int64_t)a.H * DV, t0, T);
+      if constexpr (OUT && !COMP) pq.load(Qb, (int64_t)a.H * DK, t0, T);
+    }
+    if constexpr (OUTW && COMP) {
+      const int64_t t = t0 + 32 * W + (lane & 31);
+      const bf16* qr = (const bf16*)Qb + t * a.H * DK + 8 * g2;
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          qnxt[kb][s] = t < T ? *(const bf16x8*)(qr + 32 * kb + 16 * s) : bf16x8{};
+    }
+  };
+  // log-decay of chunk n for wave 0 (tokens 2l, 2l+1), zero past T
+  float gx0 = 0.f, gx1 = 0.f;
+  auto load_g = [&](int n) {
     if (W == 0) {
-      const int64_t ta = t0 + 2 * lane, tb = ta + 1;
+      const int64_t ta = (int64_t)n * CH + 2 * lane, tb = ta + 1;
       gx0 = ta < T ? gb[ta * a.H] : 0.f;
       gx1 = tb < T ? gb[tb * a.H] : 0.f;
     }
   };
-  if (nloc > 0) prefetch(REV ? n_end - 1 : n_begin);
+  auto step_of = [&](int i) { return REV ? n_end - 1 - i : n_begin + i; };
+  if (nloc > 0) {
+    prefetch(step_of(0));
+    load_g(step_of(0));
+    if (W == 0) {
+      build_decay(&sm.dec[0], gx0, gx1);
+      if constexpr (OUT) build_utab(sm.utab[0], &sm.dec[0]);
+    }
+    if (nloc > 1) load_g(step_of(1));
+  }
 
   float decay_sum = 0.f;
   const bool store_dc = a.st_dc != nullptr, store_cd = a.st_cd != nullptr;
 
   for (int it = 0; it < nloc; ++it) {
-    const int n = REV ? n_end - 1 - it : n_begin + it;
-    __syncthreads();
-    px.template store<S::PX>(sm.x);
-    py.template store<S::PY>(sm.y);
-    if constexpr (OUT) pq.template store<S::PX>(sm.q);
-    if (W == 0) build_decay(&sm.dec, gx0, gx1);
+    const int n = step_of(it);
+    const int cur = it & 1;
+    DecayLds& dc = sm.dec[cur];
+    __syncthreads();            // previous chunk's LDS reads done; this chunk's decay tables visible
+    if constexpr (LOADER) {
+      px.template store<S::PX>(sm.x);
+      py.template store<S::PY>(sm.y);
+      if constexpr (OUT && !COMP) pq.template store<S::PQ>(sm.q);
+      if constexpr (COMP)
+        px.template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, REV ? dc.lam : dc.kap);
+    }
+    if constexpr (OUTW && COMP) {
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) { qcur[kb][0] = qnxt[kb][0]; qcur[kb][1] = qnxt[kb][1]; }
+    }
+    // next chunk's tiles go out now, a whole chunk ahead of their use
+    if (it + 1 < nloc) prefetch(step_of(it + 1));
+    if (W == 0 && it + 1 < nloc) {
+      build_decay(&sm.dec[cur ^ 1], gx0, gx1);
+      if constexpr (OUT) build_utab(sm.utab[cur ^ 1], &sm.dec[cur ^ 1]);
+    }
+    if (it + 2 < nloc) load_g(step_of(it + 2));
     if (OUT || store_dc || store_cd) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -180,114 +291,200 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
         const int d = 32 * db + (lane & 31);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const int off = d * S::PZ + 32 * cb + 8 * qq + 4 * g2;
           const f32x4 v4 = f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]};
-          if constexpr (COMP) store4_split((bf16*)sm.z + off, (bf16*)sm.zl + off, v4);
-          else store4(sm.z + off, v4);
+          if constexpr (COMP) {
+            const int off = swz96(d, 32 * cb + 8 * qq + 4 * g2);
+            store4_split((bf16*)sm.z + off, (bf16*)sm.zl + off, v4);
+          } else {
+            store4(sm.z + d * S::PZ + 32 * cb + 8 * qq + 4 * g2, v4);
+          }
         }
       }
     }
-    __syncthreads();
-    decay_sum += sm.dec.blast;
+    __syncthreads();                                   // tiles and state copy visible
+    decay_sum += dc.blast;
 
-    if constexpr (sizeof(TIn) == 2) {
-      // Per-chunk state export for the backward, bf16 MFMA-operand order.
+    if constexpr (COMP) {
+      // Per-chunk state export for the backward: [hi | lo] bf16 fragment blocks.
       if (store_dc || store_cd) {
-        // per chunk: [hi fragments | lo fragments], DK*DV bf16 each
         const int64_t base = (bh * a.n_chunks + n) * (int64_t)(2 * DK * DV);
         if (store_dc) {  // fragments (db, kc): S[d = 32db + l%32][c = 16kc + 8g + e]
           constexpr int NF = 3 * (DVS / 16);
-          for (int f = W; f < NF; f += 4) {
+          for (int f = U; f < NF; f += 4) {
             const int db = f / (DVS / 16), kcl = f % (DVS / 16);
             const int kc = c0 / 16 + kcl;
             bf16* dst = (bf16*)a.st_dc + base + ((int64_t)(db * (DV / 16) + kc) * 64 + lane) * 8;
-            *(bf16x8*)dst = frag_kcN((const bf16*)sm.z, S::PZ, 32 * db, 16 * kcl, 0);
-            *(bf16x8*)(dst + DK * DV) = frag_kcN((const bf16*)sm.zl, S::PZ, 32 * db, 16 * kcl, 0);
+            *(bf16x8*)dst = sfrag_kcN_any((const bf16*)sm.z, 32 * db, 16 * kcl, 0);
+            *(bf16x8*)(dst + DK * DV) = sfrag_kcN_any((const bf16*)sm.zl, 32 * db, 16 * kcl, 0);
           }
         }
-        if (store_cd) {  // fragments (cb, kb, s): S[d = 32kb + k(s,e)][c = 32cb + l%32]
+        if (store_cd) {  // fragments (cb, kd): S[d = 16kd + 8g + e][c = 32cb + l%32]
           constexpr int NF = NC * 6;
-          for (int f = W; f < NF; f += 4) {
-            const int cbl = f / 6, kb = (f % 6) / 2, s = f % 2;
+          for (int f = U; f < NF; f += 4) {
+            const int cbl = f / 6, kd = f % 6;
             const int cb = c0 / 32 + cbl;
-            bf16* dst = (bf16*)a.st_cd + base + ((int64_t)((cb * 3 + kb) * 2 + s) * 64 + lane) * 8;
-            *(bf16x8*)dst = frag_kr((const bf16*)sm.z, S::PZ, 32 * kb, 32 * cbl, s);
-            *(bf16x8*)(dst + DK * DV) = frag_kr((const bf16*)sm.zl, S::PZ, 32 * kb, 32 * cbl, s);
+            bf16* dst = (bf16*)a.st_cd + base + ((int64_t)(cb * 6 + kd) * 64 + lane) * 8;
+            *(bf16x8*)dst = sfrag_krN_any((const bf16*)sm.z, 32 * (kd >> 1), 32 * cbl, kd & 1);
+            *(bf16x8*)(dst + DK * DV) = sfrag_krN_any((const bf16*)sm.zl, 32 * (kd >> 1), 32 * cbl, kd & 1);
           }
         }
       }
     }
 
-    if (it + 1 < nloc) prefetch(REV ? n - 1 : n + 1);
 
-    if constexpr (OUT) {
+    if constexpr (OUTW) {
       const int il = 32 * W + (lane & 31);          // this lane's token inside the chunk
-      const float bi = sm.dec.b2[il];
-      FT qn[3][SUB], qp[3][SUB];
+      const float bi = dc.b2[il];
+      FT qn[3][SUB];
 #pragma unroll
       for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-          qn[kb][s] = frag_kcN(sm.q, S::PX, 32 * W, 32 * kb, s);
-          qp[kb][s] = frag_kcP(sm.q, S::PX, 32 * W, 32 * kb, s);
+          if constexpr (COMP) qn[kb][s] = qcur[kb][s];
+          else qn[kb][s] = frag_kcP(sm.q, S::PQ, 32 * W, 32 * kb, s);
         }
-      // Decay-masked scores P^T (keys j in rows, queries i in columns).
-      FT pf[W + 1][SUB];
-      FT pl[COMP ? W + 1 : 1][SUB];
+      // Decay-masked scores P^T (keys j in rows, queries i in columns), all
+      // key blocks at once.  Off the diagonal 2^{b_i - b_j} =
+      // 2^{b_i - b_{32W}} 2^{b_{32W} - b_j}, both factors <= 1.
+      f32x16 acc[W + 1];
 #pragma unroll
-      for (int J = 0; J <= W; ++J) {
-        f32x16 acc = {};
+      for (int J = 0; J <= W; ++J) acc[J] = f32x16{};
+      if constexpr (COMP) {
+        bf16x8 xk[2][W + 1];
+#pragma unroll
+        for (int J = 0; J <= W; ++J) xk[0][J] = sfrag_kcN((const bf16*)sm.x, 32 * J, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          const int cur = k & 1, kb = k >> 1, s = k & 1;
+          if (k + 1 < 6) {
+#pragma unroll
+            for (int J = 0; J <= W; ++J)
+              xk[cur ^ 1][J] = sfrag_kcN((const bf16*)sm.x, 32 * J, 32 * ((k + 1) >> 1), (k + 1) & 1);
+          }
+#pragma unroll
+          for (int J = 0; J <= W; ++J) acc[J] = mfma(xk[cur][J], qn[kb][s], acc[J]);
+        }
+      } else {
 #pragma unroll
         for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
           for (int s = 0; s < SUB; ++s)
-            acc = mfma(frag_kcN(sm.x, S::PX, 32 * J, 32 * kb, s), qn[kb][s], acc);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * J + out_row(r);
-          const float w = exp2f(fminf(bi - sm.dec.b2[j], 0.f));
-          acc[r] = (J < W || j <= il) ? acc[r] * w : 0.f;
+            for (int J = 0; J <= W; ++J)
+              acc[J] = mfma(frag_kcP(sm.x, S::PX, 32 * J, 32 * kb, s), qn[kb][s], acc[J]);
+      }
+      FT pf[W + 1][SUB];
+      FT pl[COMP ? W + 1 : 1][SUB];
+      const float ri = W > 0 ? exp2f(bi - dc.b2[32 * W]) : 1.f;
+#pragma unroll
+      for (int J = 0; J <= W; ++J) {
+        if (J < W) {
+          const float* u = sm.utab[cur] + utab_off(W) + 32 * J + 4 * g2;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 uu = *(const f32x4*)(u + 8 * qq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[J][4 * qq + e] *= uu[e] * ri;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * J + out_row(r);
+            const float w = exp2f(fminf(bi - dc.b2[j], 0.f));
+            acc[J][r] = j <= il ? acc[J][r] * w : 0.f;
+          }
         }
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-          if constexpr (COMP) regs_to_frag_split(acc, s, pf[J][s], pl[J][s]);
-          else pf[J][s] = acc[s];
+          if constexpr (COMP) split_tile(acc[J], s, pf[J][s], pl[J][s]);
+          else pf[J][s] = acc[J][s];
         }
       }
-      const float lam = sm.dec.lam[il];
-      const int64_t trow = (int64_t)n * CH + il;
+      // Outputs of all dv blocks at once: O^T = diag(Lambda) (Z^T Q^T) + V^T P^T.
+      f32x16 o[NC];
 #pragma unroll
-      for (int cb = 0; cb < NC; ++cb) {
-        f32x16 o = {};
+      for (int cb = 0; cb < NC; ++cb) o[cb] = f32x16{};
+      if constexpr (COMP) {
+        // Software-pipelined: the operands of step k+1 are requested before
+        // the MFMAs of step k, so LDS latency overlaps matrix-core work.
+        bf16x8 zh[2][NC], zlo[2][NC];
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+          zh[0][cb] = sfrag_krN((const bf16*)sm.z, 0, 32 * cb, 0);
+          zlo[0][cb] = sfrag_krN((const bf16*)sm.zl, 0, 32 * cb, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          const int cur = k & 1, kb = k >> 1, s = k & 1;
+          if (k + 1 < 6) {
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) {
+              zh[cur ^ 1][cb] = sfrag_krN((const bf16*)sm.z, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
+              zlo[cur ^ 1][cb] = sfrag_krN((const bf16*)sm.zl, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
+            }
+          }
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb) {
+            o[cb] = mfma(zh[cur][cb], qn[kb][s], o[cb]);
+            o[cb] = mfma(zlo[cur][cb], qn[kb][s], o[cb]);
+          }
+        }
+      } else {
 #pragma unroll
         for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
-          for (int s = 0; s < SUB; ++s) {
-            o = mfma(frag_kr(sm.z, S::PZ, 32 * kb, 32 * cb, s), qp[kb][s], o);
-            if constexpr (COMP) o = mfma(frag_kr(sm.zl, S::PZ, 32 * kb, 32 * cb, s), qp[kb][s], o);
+          for (int s = 0; s < SUB; ++s)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb)
+              o[cb] = mfma(frag_kr(sm.z, S::PZ, 32 * kb, 32 * cb, s), qn[kb][s], o[cb]);
+      }
+      const float lam = dc.lam[il];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) o[cb] *= lam;
+      if constexpr (COMP) {
+        constexpr int NK = 2 * (W + 1);                 // (J, s) steps
+        bf16x8 yv[2][NC];
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) yv[0][cb] = sfrag_kr((const bf16*)sm.y, 0, 32 * cb, 0);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const int cur = k & 1, J = k >> 1, s = k & 1;
+          if (k + 1 < NK) {
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb)
+              yv[cur ^ 1][cb] = sfrag_kr((const bf16*)sm.y, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
           }
-        o *= lam;
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb) {
+            o[cb] = mfma(yv[cur][cb], pf[J][s], o[cb]);
+            o[cb] = mfma(yv[cur][cb], pl[J][s], o[cb]);
+          }
+        }
+      } else {
 #pragma unroll
         for (int J = 0; J <= W; ++J)
 #pragma unroll
-          for (int s = 0; s < SUB; ++s) {
-            const FT ay = frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s);
-            o = mfma(ay, pf[J][s], o);
-            if constexpr (COMP) o = mfma(ay, pl[J][s], o);
-          }
-        if (trow < T) {
-          TOut* op = (TOut*)a.O + (((int64_t)b * T + trow) * a.H + h) * DV + c0 + 32 * cb + 4 * g2;
+          for (int s = 0; s < SUB; ++s)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb)
+              o[cb] = mfma(frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s), pf[J][s], o[cb]);
+      }
+      const int64_t trow = (int64_t)n * CH + il;
+      if (trow < T) {
+        TOut* op = (TOut*)a.O + (((int64_t)b * T + trow) * a.H + h) * DV + c0 + 4 * g2;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
-            store4(op + 8 * qq, f32x4{o[4 * qq], o[4 * qq + 1], o[4 * qq + 2], o[4 * qq + 3]});
-        }
+            store4(op + 32 * cb + 8 * qq,
+                   f32x4{o[cb][4 * qq], o[cb][4 * qq + 1], o[cb][4 * qq + 2], o[cb][4 * qq + 3]});
       }
     }
 
     // State update: Z^T = Gamma Z^T + Y^T (w X), contraction over the chunk's tokens.
     if constexpr (NT > 0) {
-      const float gam = sm.dec.gam;
-      const float* wts = REV ? sm.dec.lam : sm.dec.kap;
+      const float gam = dc.gam;
+      const float* wts = REV ? dc.lam : dc.kap;
 #pragma unroll
       for (int t = 0; t < NT; ++t) z[t] *= gam;
       constexpr int DB_LO = (NT >= 3) ? 0 : (T0 % 3);
@@ -300,16 +497,21 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 #pragma unroll
           for (int k = 0; k < DB_N; ++k) {
             const int db = (DB_LO + k) % 3;
-            if constexpr (COMP)
-              scale_k_split(frag_kr(sm.x, S::PX, 32 * J, 32 * db, s), wts + 32 * J, s, bx[db], bl[db]);
-            else
+            if constexpr (COMP) {
+              bx[db] = sfrag_kr((const bf16*)sm.xh, 32 * J, 32 * db, s);
+              bl[db] = sfrag_kr((const bf16*)sm.xl, 32 * J, 32 * db, s);
+            } else {
               bx[db] = scale_k(frag_kr(sm.x, S::PX, 32 * J, 32 * db, s), wts + 32 * J, s);
+            }
           }
           FT ay = {};
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
-            if (t == 0 || db == 0) ay = frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s);
+            if (t == 0 || db == 0) {
+              if constexpr (COMP) ay = sfrag_kr((const bf16*)sm.y, 32 * J, 32 * cb, s);
+              else ay = frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s);
+            }
             z[t] = mfma(ay, bx[db], z[t]);
             if constexpr (COMP) z[t] = mfma(ay, bl[db], z[t]);
           }
@@ -336,7 +538,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 }
 
 template <class TIn, class TOut, int NC, int MODE>
-__global__ void __launch_bounds__(256, 1) walk_kernel(WalkArgs a) {
+__global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkArgs a) {
   __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
   // Work item order: slice fastest, then segment, head, batch.  Consecutive
   // items are placed on the same XCD (the dispatcher deals workgroups to the
@@ -355,7 +557,17 @@ __global__ void __launch_bounds__(256, 1) walk_kernel(WalkArgs a) {
     case 0: walk_wave<TIn, TOut, NC, MODE, 0>(a, sm, b, h, slice, seg); break;
     case 1: walk_wave<TIn, TOut, NC, MODE, 1>(a, sm, b, h, slice, seg); break;
     case 2: walk_wave<TIn, TOut, NC, MODE, 2>(a, sm, b, h, slice, seg); break;
-    default: walk_wave<TIn, TOut, NC, MODE, 3>(a, sm, b, h, slice, seg); break;
+    case 3: walk_wave<TIn, TOut, NC, MODE, 3>(a, sm, b, h, slice, seg); break;
+    default:
+      if constexpr (WalkShape<MODE>::WAVES == 8) {
+        switch (threadIdx.x >> 6) {
+          case 4: walk_wave<TIn, TOut, NC, MODE, 4>(a, sm, b, h, slice, seg); break;
+          case 5: walk_wave<TIn, TOut, NC, MODE, 5>(a, sm, b, h, slice, seg); break;
+          case 6: walk_wave<TIn, TOut, NC, MODE, 6>(a, sm, b, h, slice, seg); break;
+          default: walk_wave<TIn, TOut, NC, MODE, 7>(a, sm, b, h, slice, seg); break;
+        }
+      }
+      break;
   }
 }
 
@@ -381,7 +593,7 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(float* buf, const float* 
 // ---------------------------------------------------------------------------
 template <class TIn, class TOut, int NC, int MODE>
 static hipError_t launch_one(const WalkArgs& a, int nwg, hipStream_t st) {
-  hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE>), dim3(nwg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE>), dim3(nwg), dim3(WalkShape<MODE>::THREADS), 0, st, a);
   return hipGetLastError();
 }
 
