@@ -260,8 +260,9 @@ __global__ void __launch_bounds__(256, 1) bwd_chunk_kernel(BwdArgs a) {
   if (threadIdx.x < 64) {
     const int l = threadIdx.x;
     const float* gb = a.g + b * T * a.H + h;
-    const int64_t ta = t0 + 2 * l, tb = ta + 1;
-    build_decay(&sm.dec, ta < T ? gb[ta * a.H] : 0.f, tb < T ? gb[tb * a.H] : 0.f);
+    const int64_t ta = t0 + 2 * l, tb = ta + 1, tc = t0 + 127 - 2 * l, td = tc - 1;
+    build_decay(&sm.dec, ta < T ? gb[ta * a.H] : 0.f, tb < T ? gb[tb * a.H] : 0.f, tc < T ? gb[tc * a.H] : 0.f,
+                td < T ? gb[td * a.H] : 0.f);
   }
   __syncthreads();
   switch (threadIdx.x >> 6) {

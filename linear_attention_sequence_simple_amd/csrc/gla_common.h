@@ -297,6 +297,26 @@ __device__ __forceinline__ float wave_incl_rscan(float x) {
   return x;
 }
 
+// DPP lane moves (gfx9 encodings): row_shr:n = 0x110+n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143, wave_shr:1 = 0x138.  Lanes without a source read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true));
+}
+// Inclusive prefix sum over the 64 lanes: shifts 1, 2, 4, 8 inside each row
+// of 16 lanes, then the row totals are broadcast into the later rows.
+__device__ __forceinline__ float wave_scan_dpp(float x) {
+  x += dpp_mov<0x111, 0xf>(x);
+  x += dpp_mov<0x112, 0xf>(x);
+  x += dpp_mov<0x114, 0xf>(x);
+  x += dpp_mov<0x118, 0xf>(x);
+  x += dpp_mov<0x142, 0xa>(x);
+  x += dpp_mov<0x143, 0xc>(x);
+  return x;
+}
+// Value of the previous lane (0 for lane 0).
+__device__ __forceinline__ float wave_shr1(float x) { return dpp_mov<0x138, 0xf>(x); }
+
 // Chunk decay tables in LDS, from the chunk's log-decay.  With b_i the
 // inclusive running sum of the clamped log-decay (in log2 units):
 //   b2[i]  = b_i,  lam[i] = 2^{b_i},  kap[i] = 2^{b_last - b_i},  gam = 2^{b_last}
@@ -308,29 +328,42 @@ struct DecayLds {
   float blast;
 };
 
-// Called by one whole wave; x0, x1 are the log-decays of tokens 2l and 2l+1
-// (0 for padded tokens).  The prefix sums give b and Lambda; kappa comes from
-// a separate suffix sum so that it does not inherit the rounding of
-// b_last - b_j (kappa of the last real token is exactly 1).
-__device__ __forceinline__ void build_decay(DecayLds* d, float x0, float x1) {
+// Called by one whole wave.  x0, x1: log-decays of tokens 2l and 2l+1;
+// m0, m1: of tokens 127-2l and 126-2l (0 for padded tokens).  kappa comes
+// from a prefix sum over the mirrored tokens (a suffix sum), so it does not
+// inherit the rounding of b_last - b_j; kappa of the last real token is 1.
+// If utab is given, also utab[U(I) + j] = 2^{b_{32I} - b_j} for j < 32I,
+// I = 1..3, U = 0, 32, 96 (decay factors between 32-token blocks).
+__device__ __forceinline__ void build_decay(DecayLds* d, float x0, float x1, float m0, float m1,
+                                            float* utab = nullptr) {
   const int l = lane_id();
   x0 = fmaxf(x0, G_MIN) * LOG2E;
   x1 = fmaxf(x1, G_MIN) * LOG2E;
-  const float pr = wave_incl_scan(x0 + x1);          // sum over tokens <= 2l+1
-  float pr_ex = __shfl_up(pr, 1, 64);                 // sum over tokens < 2l
-  if (l == 0) pr_ex = 0.f;
-  const float sr = wave_incl_rscan(x0 + x1);          // sum over tokens >= 2l
-  float sr_ex = __shfl_down(sr, 1, 64);               // sum over tokens > 2l+1
-  if (l == 63) sr_ex = 0.f;
+  m0 = fmaxf(m0, G_MIN) * LOG2E;
+  m1 = fmaxf(m1, G_MIN) * LOG2E;
+  const float pr = wave_scan_dpp(x0 + x1);            // sum over tokens <= 2l+1
+  const float pr_ex = wave_shr1(pr);                  // sum over tokens < 2l
+  const float sr = wave_scan_dpp(m0 + m1);            // sum over tokens >= 126-2l
+  const float sr_ex = wave_shr1(sr);                  // sum over tokens > 127-2l
   const float b0 = pr_ex + x0, b1 = pr;
-  const float blast = __shfl(pr, 63, 64);
+  const float blast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), 63));
   d->b2[2 * l] = b0;
   d->b2[2 * l + 1] = b1;
   d->lam[2 * l] = exp2f(b0);
   d->lam[2 * l + 1] = exp2f(b1);
-  d->kap[2 * l] = exp2f(sr_ex + x1);
-  d->kap[2 * l + 1] = exp2f(sr_ex);
+  d->kap[127 - 2 * l] = exp2f(sr_ex);
+  d->kap[126 - 2 * l] = exp2f(sr_ex + m0);
   if (l == 0) { d->gam = exp2f(blast); d->blast = blast; }
+  if (utab) {
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+      // b_{32I} is b0 of lane 16I
+      const float bref = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b0), 16 * I));
+      const int off = I == 1 ? 0 : I == 2 ? 32 : 96;
+      if (2 * l < 32 * I) utab[off + 2 * l] = exp2f(bref - b0);
+      if (2 * l + 1 < 32 * I) utab[off + 2 * l + 1] = exp2f(bref - b1);
+    }
+  }
 }
 
 }  // namespace gla

@@ -25,6 +25,8 @@
 // decay-weighted keys) are not: each is split into a bf16 value and its bf16
 // residual and multiplied as two MFMAs (error-compensated 16-bit products, as
 // the HEAL page "Problema" / "HEAL-B" sections describe for bf16 inference).
+#include <type_traits>
+
 #include "gla_common.h"
 #include "gla_kernels.h"
 
@@ -44,7 +46,8 @@ struct Own {
   // grows with u.
   static constexpr int count(int u) {
     if (OUT) {
-      if (NC == 3) return u == 0 ? 4 : u == 1 ? 3 : u == 2 ? 2 : 0;
+      // every SIMD gets a second active wave to overlap the output wave's stalls
+      if (NC == 3) return u == 0 ? 3 : 2;
       if (NC == 2) return u == 0 ? 3 : u == 1 ? 2 : u == 2 ? 1 : 0;
     } else {
       if (NC == 3) return u == 0 ? 3 : 2;
@@ -90,21 +93,6 @@ struct WalkSmem {
 };
 
 __device__ __forceinline__ int utab_off(int I) { return I == 1 ? 0 : I == 2 ? 32 : 96; }
-
-// Block-boundary decay factors, by the wave that built the decay tables (its
-// lanes hold b of tokens 2l, 2l+1).
-__device__ __forceinline__ void build_utab(float* utab, const DecayLds* d) {
-  const int l = lane_id();
-#pragma unroll
-  for (int I = 1; I < 4; ++I) {
-    const float bref = d->b2[32 * I];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = 2 * l + e;
-      if (j < 32 * I) utab[utab_off(I) + j] = exp2f(bref - d->b2[j]);
-    }
-  }
-}
 
 // Rows [t0, t0+128) of a [B,T,H,D] tensor, columns [col0, col0+W), as 16-byte
 // pieces held in registers; rows past T read as zero.
@@ -216,18 +204,29 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     }
   }
 
-  TileRegs<TIn, DK, NTHR> px;
-  TileRegs<TIn, DVS, NTHR> py;
-  TileRegs<TIn, (OUT && !COMP) ? DK : 8, NTHR> pq;
-  // bf16 queries of this output wave's 32 tokens, as plain-order MFMA B operands
+  // DEPTH register buffers of chunk tiles: chunk it+DEPTH is requested while
+  // chunk it is processed.  The state-only bf16 walks have little arithmetic
+  // to hide memory behind and the registers for two buffers; the others keep
+  // one.  The chunk loop is unrolled by two so that each buffer keeps its
+  // registers (copies would force early waits).
+  constexpr int DEPTH = (!OUT && COMP) ? 2 : 1;
+  TileRegs<TIn, DK, NTHR> px[DEPTH];
+  TileRegs<TIn, DVS, NTHR> py[DEPTH];
+  TileRegs<TIn, (OUT && !COMP) ? DK : 8, NTHR> pq[DEPTH];
+  // bf16 queries of this output wave's 32 tokens, as plain-order MFMA B
+  // operands: the current chunk's and, in flight, the next chunk's
   bf16x8 qcur[(OUTW && COMP) ? 3 : 1][2], qnxt[(OUTW && COMP) ? 3 : 1][2];
-  auto prefetch = [&](int n) {
+  auto prefetch = [&](auto bc, int n) {
+    constexpr int B = decltype(bc)::value % DEPTH;
     const int t0 = n * CH;
     if constexpr (LOADER) {
-      px.load(Xb, (int64_t)a.H * DK, t0, T);
-      py.load(Yb, (int64_t)a.H * DV, t0, T);
-      if constexpr (OUT && !COMP) pq.load(Qb, (int64_t)a.H * DK, t0, T);
+      px[B].load(Xb, (int64_t)a.H * DK, t0, T);
+      py[B].load(Yb, (int64_t)a.H * DV, t0, T);
+      if constexpr (OUT && !COMP) pq[B].load(Qb, (int64_t)a.H * DK, t0, T);
     }
+  };
+  auto prefetch_q = [&](int n) {
+    const int t0 = n * CH;
     if constexpr (OUTW && COMP) {
       const int64_t t = t0 + 32 * W + (lane & 31);
       const bf16* qr = (const bf16*)Qb + t * a.H * DK + 8 * g2;
@@ -238,52 +237,54 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
           qnxt[kb][s] = t < T ? *(const bf16x8*)(qr + 32 * kb + 16 * s) : bf16x8{};
     }
   };
-  // log-decay of chunk n for wave 0 (tokens 2l, 2l+1), zero past T
-  float gx0 = 0.f, gx1 = 0.f;
+  constexpr std::integral_constant<int, 0> I0{};
+  constexpr std::integral_constant<int, 1> I1{};
+  // log-decay of chunk n for wave 0: tokens 2l, 2l+1 and the mirrored
+  // 127-2l, 126-2l; zero past T
+  float gx0 = 0.f, gx1 = 0.f, gm0 = 0.f, gm1 = 0.f;
   auto load_g = [&](int n) {
     if (W == 0) {
-      const int64_t ta = (int64_t)n * CH + 2 * lane, tb = ta + 1;
+      const int64_t t0 = (int64_t)n * CH;
+      const int64_t ta = t0 + 2 * lane, tb = ta + 1, tc = t0 + 127 - 2 * lane, td = tc - 1;
       gx0 = ta < T ? gb[ta * a.H] : 0.f;
       gx1 = tb < T ? gb[tb * a.H] : 0.f;
+      gm0 = tc < T ? gb[tc * a.H] : 0.f;
+      gm1 = td < T ? gb[td * a.H] : 0.f;
     }
   };
   auto step_of = [&](int i) { return REV ? n_end - 1 - i : n_begin + i; };
   if (nloc > 0) {
-    prefetch(step_of(0));
+    prefetch(I0, step_of(0));
+    prefetch_q(step_of(0));
+    if (DEPTH == 2 && nloc > 1) prefetch(I1, step_of(1));
     load_g(step_of(0));
-    if (W == 0) {
-      build_decay(&sm.dec[0], gx0, gx1);
-      if constexpr (OUT) build_utab(sm.utab[0], &sm.dec[0]);
-    }
+    if (W == 0) build_decay(&sm.dec[0], gx0, gx1, gm0, gm1, OUT ? sm.utab[0] : nullptr);
     if (nloc > 1) load_g(step_of(1));
   }
 
   float decay_sum = 0.f;
   const bool store_dc = a.st_dc != nullptr, store_cd = a.st_cd != nullptr;
 
-  for (int it = 0; it < nloc; ++it) {
+  auto body = [&](auto bc, int it) {
+    constexpr int B = decltype(bc)::value % DEPTH;    // register buffer of this chunk
     const int n = step_of(it);
-    const int cur = it & 1;
+    const int cur = it & 1;                            // decay-table buffer of this chunk
     DecayLds& dc = sm.dec[cur];
     __syncthreads();            // previous chunk's LDS reads done; this chunk's decay tables visible
     if constexpr (LOADER) {
-      px.template store<S::PX>(sm.x);
-      py.template store<S::PY>(sm.y);
-      if constexpr (OUT && !COMP) pq.template store<S::PQ>(sm.q);
+      px[B].template store<S::PX>(sm.x);
+      py[B].template store<S::PY>(sm.y);
+      if constexpr (OUT && !COMP) pq[B].template store<S::PQ>(sm.q);
       if constexpr (COMP)
-        px.template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, REV ? dc.lam : dc.kap);
+        px[B].template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, REV ? dc.lam : dc.kap);
     }
+    // chunk it+DEPTH goes into this buffer now that it is staged
+    if (it + DEPTH < nloc) prefetch(bc, step_of(it + DEPTH));
     if constexpr (OUTW && COMP) {
 #pragma unroll
       for (int kb = 0; kb < 3; ++kb) { qcur[kb][0] = qnxt[kb][0]; qcur[kb][1] = qnxt[kb][1]; }
     }
-    // next chunk's tiles go out now, a whole chunk ahead of their use
-    if (it + 1 < nloc) prefetch(step_of(it + 1));
-    if (W == 0 && it + 1 < nloc) {
-      build_decay(&sm.dec[cur ^ 1], gx0, gx1);
-      if constexpr (OUT) build_utab(sm.utab[cur ^ 1], &sm.dec[cur ^ 1]);
-    }
-    if (it + 2 < nloc) load_g(step_of(it + 2));
+    if (it + 1 < nloc) prefetch_q(step_of(it + 1));
     if (OUT || store_dc || store_cd) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -489,35 +490,70 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       for (int t = 0; t < NT; ++t) z[t] *= gam;
       constexpr int DB_LO = (NT >= 3) ? 0 : (T0 % 3);
       constexpr int DB_N = (NT >= 3) ? 3 : NT;   // contiguous db range (mod 3) when NT < 3
+      if constexpr (COMP) {
+        // Software-pipelined over the 8 (J, s) contraction steps.
+        constexpr int CB_LO = T0 / 3, NCB = (T0 + NT - 1) / 3 - CB_LO + 1;
+        bf16x8 bx[2][3], bl[2][3], ay[2][NCB];
+        auto load_ops = [&](int buf, int k) {
+          const int J = k >> 1, s = k & 1;
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-#pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-          FT bx[3], bl[3];
-#pragma unroll
-          for (int k = 0; k < DB_N; ++k) {
-            const int db = (DB_LO + k) % 3;
-            if constexpr (COMP) {
-              bx[db] = sfrag_kr((const bf16*)sm.xh, 32 * J, 32 * db, s);
-              bl[db] = sfrag_kr((const bf16*)sm.xl, 32 * J, 32 * db, s);
-            } else {
-              bx[db] = scale_k(frag_kr(sm.x, S::PX, 32 * J, 32 * db, s), wts + 32 * J, s);
-            }
+          for (int q = 0; q < DB_N; ++q) {
+            const int db = (DB_LO + q) % 3;
+            bx[buf][db] = sfrag_kr((const bf16*)sm.xh, 32 * J, 32 * db, s);
+            bl[buf][db] = sfrag_kr((const bf16*)sm.xl, 32 * J, 32 * db, s);
           }
-          FT ay = {};
+#pragma unroll
+          for (int c = 0; c < NCB; ++c) ay[buf][c] = sfrag_kr((const bf16*)sm.y, 32 * J, 32 * (CB_LO + c), s);
+        };
+        load_ops(0, 0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int cur = k & 1;
+          if (k + 1 < 8) load_ops(cur ^ 1, k + 1);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
-            if (t == 0 || db == 0) {
-              if constexpr (COMP) ay = sfrag_kr((const bf16*)sm.y, 32 * J, 32 * cb, s);
-              else ay = frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s);
+            z[t] = mfma(ay[cur][cb - CB_LO], bx[cur][db], z[t]);
+            z[t] = mfma(ay[cur][cb - CB_LO], bl[cur][db], z[t]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+#pragma unroll
+          for (int s = 0; s < SUB; ++s) {
+            FT bx[3];
+#pragma unroll
+            for (int k = 0; k < DB_N; ++k) {
+              const int db = (DB_LO + k) % 3;
+              bx[db] = scale_k(frag_kr(sm.x, S::PX, 32 * J, 32 * db, s), wts + 32 * J, s);
             }
-            z[t] = mfma(ay, bx[db], z[t]);
-            if constexpr (COMP) z[t] = mfma(ay, bl[db], z[t]);
+            FT ay = {};
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
+              if (t == 0 || db == 0) ay = frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s);
+              z[t] = mfma(ay, bx[db], z[t]);
+            }
           }
         }
       }
     }
+    // Decay tables of the next chunk, after this wave's arithmetic so that
+    // its log-decay loads (issued an iteration ago) have arrived; they are
+    // published by the next iteration's first barrier.
+    if (W == 0 && it + 1 < nloc) {
+      build_decay(&sm.dec[cur ^ 1], gx0, gx1, gm0, gm1, OUT ? sm.utab[cur ^ 1] : nullptr);
+      if (it + 2 < nloc) load_g(step_of(it + 2));
+    }
+  };
+  if constexpr (DEPTH == 2) {
+    for (int it = 0; it < nloc; it += 2) {
+      body(I0, it);
+      if (it + 1 < nloc) body(I1, it + 1);
+    }
+  } else {
+    for (int it = 0; it < nloc; ++it) body(I0, it);
   }
 
   // ---- final state
