@@ -15,11 +15,11 @@
 // (derivative through the running sum of the log-decay): this kernel writes
 // the in-chunk suffix sums and the chunk totals; dg_finish adds the rest.
 //
-// One workgroup (4 waves) per (batch, head, chunk).  Wave w owns the 32
-// tokens 32w..32w+31 as the column block of its result tiles:
-//   dV^T[:, w], dQ^T[:, w], dK^T[:, w]  (c or d rows, tokens in columns),
-// so each lane ends up with one token and the q.dq / k.dk dot products need
-// only a sum over its registers and one exchange with the other lane group.
+// One workgroup (8 waves) per (batch, head, chunk).  Token block w (32
+// tokens) is the column block of the result tiles dV^T[:, w] (wave w) and
+// dQ^T[:, w], dK^T[:, w] (wave 4+w), so each lane ends up with one token and
+// the q.dq / k.dk dot products need only a sum over its registers and one
+// exchange with the other lane group.
 // The masked scores and the stored states enter the products as compensated
 // bf16 pairs (value + residual, two MFMAs); q, k, v, dO are exact bf16.
 #include "gla_common.h"
@@ -27,222 +27,232 @@
 
 namespace gla {
 
+// Chunk tiles in LDS: q, k [128][96] and the two 96-wide halves of v, dO,
+// all in the swizzled unpadded layout (swz96), so the row reads and the
+// transposed reads are free of bank conflicts.
 struct BwdSmem {
-  static constexpr int PX = DK + 8;
-  static constexpr int PY = DV + 8;
-  bf16 q[CH * PX];
-  bf16 k[CH * PX];
-  bf16 v[CH * PY];
-  bf16 dO[CH * PY];
+  bf16 q[CH * 96];
+  bf16 k[CH * 96];
+  bf16 v[2][CH * 96];
+  bf16 dO[2][CH * 96];
   DecayLds dec;
   float r[CH];
 };
 
-__device__ __forceinline__ void load_tile_lds(bf16* lds, int pitch, const bf16* base, int64_t row_stride,
-                                              int width, int64_t t0, int64_t T) {
-  const int ppr = width / 8;
-  const int np = CH * ppr;
-  for (int p = threadIdx.x; p < np; p += 256) {
-    const int row = p / ppr, cp = p % ppr;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (t0 + row < T) val = *(const uint4*)(base + (t0 + row) * row_stride + cp * 8);
-    *(uint4*)(lds + row * pitch + cp * 8) = val;
+// One chunk tile [128][W] of a [B,T,H,D] tensor into LDS (as 96-wide halves),
+// rows past T as zero; all 512 threads.
+template <int WIDTH>
+__device__ __forceinline__ void stage_tile(bf16* lds, const bf16* base, int64_t row_stride, int64_t t0, int64_t T) {
+  constexpr int PPR = WIDTH / 8, NP = CH * PPR, PER = NP / 512;
+  uint4 r[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = threadIdx.x + 512 * i, row = p / PPR, cp = p % PPR;
+    r[i] = (t0 + row < T) ? *(const uint4*)(base + (t0 + row) * row_stride + cp * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = threadIdx.x + 512 * i, row = p / PPR, cp = p % PPR;
+    *(uint4*)(lds + (cp / 12) * (CH * 96) + swz96(row, (cp % 12) * 8)) = r[i];
   }
 }
 
 __device__ __forceinline__ bf16x8 gfrag(const bf16* base, int f) {
   return *(const bf16x8*)(base + ((int64_t)f * 64 + lane_id()) * 8);
 }
+// 32-column blocks of a 192-wide tile stored as two swizzled halves
+__device__ __forceinline__ const bf16* half_of(const bf16 (*t)[CH * 96], int col0) { return t[col0 / 96]; }
 
-// Masked score tiles of one column block: rows in [32*R0, 128) (or [0, 32*(W+1))),
-// held as compensated bf16 operand pairs for the next contraction over rows.
+// Masked score tile rows in register order, as compensated operand pairs.
 struct PairFrag {
   bf16x8 hi[2], lo[2];
 };
 
+// ---- dV wave: P (query rows i >= 32W, key column tl) and dV^T[:, W]
 template <class TOut, int W>
-__device__ __forceinline__ void bwd_wave(const BwdArgs& a, BwdSmem& sm, int64_t bh, int64_t b, int h, int n) {
-  constexpr int PX = BwdSmem::PX, PY = BwdSmem::PY;
-  const int lane = lane_id();
-  const int g2 = lane >> 5;
-  const int tl = 32 * W + (lane & 31);            // this lane's token inside the chunk
-  const int64_t T = a.T;
-  const int64_t trow = (int64_t)n * CH + tl;
-  const bool valid = trow < T;
+__device__ __forceinline__ void bwd_dv_wave(const BwdArgs& a, BwdSmem& sm, const bf16* dScd, int64_t tok, bool valid) {
+  const int lane = lane_id(), g2 = lane >> 5;
+  const int tl = 32 * W + (lane & 31);
   const float b_t = sm.dec.b2[tl];
-  // per chunk: [hi fragments | lo fragments]
-  const int64_t frag_base = (bh * a.n_chunks + n) * (int64_t)(2 * DK * DV);
-  const bf16* Sdc = (const bf16*)a.s_dc + frag_base;
-  const bf16* dSdc = (const bf16*)a.ds_dc + frag_base;
-  const bf16* dScd = (const bf16*)a.ds_cd + frag_base;
   const float kap = sm.dec.kap[tl];
-  const float lam = sm.dec.lam[tl];
-  const int64_t tok = ((int64_t)b * T + trow) * a.H + h;
-
-  // ---- phase 1: P (query rows i >= 32W, key column tl) and dV^T[:, W]
-  {
-    PairFrag P[4];
+  PairFrag P[4];
 #pragma unroll
-    for (int I = W; I < 4; ++I) {
-      f32x16 ap = {};
+  for (int I = W; I < 4; ++I) {
+    f32x16 ap = {};
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
+    for (int k = 0; k < 6; ++k)
+      ap = mfma(sfrag_kcN(sm.q, 32 * I, 32 * (k >> 1), k & 1), sfrag_kcN(sm.k, 32 * W, 32 * (k >> 1), k & 1), ap);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          ap = mfma(frag_kcN(sm.q, PX, 32 * I, 32 * kb, s), frag_kcN(sm.k, PX, 32 * W, 32 * kb, s), ap);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * I + out_row(r);
-        const float w = exp2f(fminf(sm.dec.b2[i] - b_t, 0.f));
-        ap[r] = ((I > W) || (tl <= i)) ? ap[r] * w : 0.f;
-      }
-      regs_to_frag_split(ap, 0, P[I].hi[0], P[I].lo[0]);
-      regs_to_frag_split(ap, 1, P[I].hi[1], P[I].lo[1]);
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * I + out_row(r);
+      const float w = exp2f(fminf(sm.dec.b2[i] - b_t, 0.f));
+      ap[r] = ((I > W) || (tl <= i)) ? ap[r] * w : 0.f;
     }
+    split_tile(ap, 0, P[I].hi[0], P[I].lo[0]);
+    split_tile(ap, 1, P[I].hi[1], P[I].lo[1]);
+  }
+  // keys of this block as B operands of the state term (plain order over d)
+  bf16x8 kB[6];
 #pragma unroll
-    for (int cb = 0; cb < 6; ++cb) {
-      f32x16 acc = {};
+  for (int k = 0; k < 6; ++k) kB[k] = sfrag_kcN(sm.k, 32 * W, 32 * (k >> 1), k & 1);
+  // state-gradient fragments, 4 steps ahead over the 36 (c-block, d-step) pairs
+  constexpr int L = 4;
+  bf16x8 fh[36], fl[36];
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
+  for (int f = 0; f < L; ++f) { fh[f] = gfrag(dScd, f); fl[f] = gfrag(dScd + DK * DV, f); }
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 bk = frag_kcN(sm.k, PX, 32 * W, 32 * kb, s);
-          const int f = cb * 6 + kb * 2 + s;
-          acc = mfma(gfrag(dScd, f), bk, acc);
-          acc = mfma(gfrag(dScd + DK * DV, f), bk, acc);
-        }
-      acc *= kap;
+  for (int cb = 0; cb < 6; ++cb) {
+    f32x16 acc = {};
 #pragma unroll
-      for (int I = W; I < 4; ++I)
+    for (int k = 0; k < 6; ++k) {
+      const int f = cb * 6 + k;
+      if (f + L < 36) { fh[f + L] = gfrag(dScd, f + L); fl[f + L] = gfrag(dScd + DK * DV, f + L); }
+      acc = mfma(fh[f], kB[k], acc);
+      acc = mfma(fl[f], kB[k], acc);
+    }
+    acc *= kap;
+    const bf16* dOh = half_of(sm.dO, 32 * cb);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 ad = frag_kr(sm.dO, PY, 32 * I, 32 * cb, s);
-          acc = mfma(ad, P[I].hi[s], acc);
-          acc = mfma(ad, P[I].lo[s], acc);
-        }
-      if (valid) {
-        TOut* p = (TOut*)a.dv + tok * DV + 32 * cb + 4 * g2;
+    for (int I = W; I < 4; ++I)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          store4(p + 8 * qq, f32x4{acc[4 * qq], acc[4 * qq + 1], acc[4 * qq + 2], acc[4 * qq + 3]});
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 ad = sfrag_kr(dOh, 32 * I, (32 * cb) % 96, s);
+        acc = mfma(ad, P[I].hi[s], acc);
+        acc = mfma(ad, P[I].lo[s], acc);
       }
+    if (valid) {
+      TOut* p = (TOut*)a.dv + tok * DV + 32 * cb + 4 * g2;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        store4(p + 8 * qq, f32x4{acc[4 * qq], acc[4 * qq + 1], acc[4 * qq + 2], acc[4 * qq + 3]});
     }
   }
+}
 
-  // ---- phase 2: dP^T (key rows j <= block W, query column tl) and dQ^T[:, W]
-  float rq = 0.f;
-  {
-    PairFrag D[4];
+// State terms of dQ^T or dK^T for the three d-blocks: sum over the 12
+// 16-wide c steps of fragments (hi, lo) from the workspace times a 192-wide
+// LDS operand (rows of this wave's tokens), with the global fragments 4 steps
+// ahead over the 36 (d-block, c-step) pairs.
+__device__ __forceinline__ void state_terms(const bf16* frag, const bf16 (*y)[CH * 96], int row0, f32x16 (&acc)[3]) {
+  constexpr int L = 4;
+  bf16x8 fh[36], fl[36];
 #pragma unroll
-    for (int J = 0; J <= W; ++J) {
-      f32x16 ad = {};
+  for (int f = 0; f < L; ++f) { fh[f] = gfrag(frag, f); fl[f] = gfrag(frag + DK * DV, f); }
 #pragma unroll
-      for (int kb = 0; kb < 6; ++kb)
+  for (int db = 0; db < 3; ++db) {
+    acc[db] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          ad = mfma(frag_kcN(sm.v, PY, 32 * J, 32 * kb, s), frag_kcN(sm.dO, PY, 32 * W, 32 * kb, s), ad);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = 32 * J + out_row(r);
-        const float w = exp2f(fminf(b_t - sm.dec.b2[j], 0.f));
-        ad[r] = ((J < W) || (j <= tl)) ? ad[r] * w : 0.f;
-      }
-      regs_to_frag_split(ad, 0, D[J].hi[0], D[J].lo[0]);
-      regs_to_frag_split(ad, 1, D[J].hi[1], D[J].lo[1]);
+    for (int k = 0; k < 12; ++k) {
+      const int f = db * 12 + k;
+      if (f + L < 36) { fh[f + L] = gfrag(frag, f + L); fl[f + L] = gfrag(frag + DK * DV, f + L); }
+      const int c0 = 32 * (k >> 1);
+      const bf16x8 bo = sfrag_kcN(half_of(y, c0), row0, c0 % 96, k & 1);
+      acc[db] = mfma(fh[f], bo, acc[db]);
+      acc[db] = mfma(fl[f], bo, acc[db]);
     }
+  }
+}
+
+// Masked dP^T tile (key rows of block J, query column tl) when TRANSPOSED,
+// else the masked dP tile (query rows of block J, key column tl), as a
+// compensated operand pair.
+template <bool TRANSPOSED>
+__device__ __forceinline__ PairFrag dp_tile(const BwdSmem& sm, int J, int W, int tl, float b_t) {
+  const bf16(*ra)[CH * 96] = TRANSPOSED ? sm.v : sm.dO;
+  const bf16(*rb)[CH * 96] = TRANSPOSED ? sm.dO : sm.v;
+  f32x16 ad = {};
+#pragma unroll
+  for (int k = 0; k < 12; ++k) {
+    const int c0 = 32 * (k >> 1);
+    ad = mfma(sfrag_kcN(half_of(ra, c0), 32 * J, c0 % 96, k & 1), sfrag_kcN(half_of(rb, c0), 32 * W, c0 % 96, k & 1), ad);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = 32 * J + out_row(r);
+    // dP^T[j][tl] needs j <= tl, weight 2^(b_tl - b_j); dP[j][tl] needs tl <= j
+    const float w = TRANSPOSED ? exp2f(fminf(b_t - sm.dec.b2[j], 0.f)) : exp2f(fminf(sm.dec.b2[j] - b_t, 0.f));
+    const bool keep = TRANSPOSED ? ((J < W) || (j <= tl)) : ((J > W) || (tl <= j));
+    ad[r] = keep ? ad[r] * w : 0.f;
+  }
+  PairFrag D;
+  split_tile(ad, 0, D.hi[0], D.lo[0]);
+  split_tile(ad, 1, D.hi[1], D.lo[1]);
+  return D;
+}
+
+// ---- dQ/dK wave: dP^T -> dQ^T[:, W], dP -> dK^T[:, W], and q.dq - k.dk
+template <class TOut, int W>
+__device__ __forceinline__ void bwd_dqk_wave(const BwdArgs& a, BwdSmem& sm, const bf16* Sdc, const bf16* dSdc,
+                                             int64_t tok, bool valid) {
+  const int lane = lane_id(), g2 = lane >> 5;
+  const int tl = 32 * W + (lane & 31);
+  const float b_t = sm.dec.b2[tl];
+  float r = 0.f;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    // part 0: dQ^T = diag(Lambda) (S_n dO^T-term) + K^T dP^T;  part 1: dK^T = diag(kappa) (...) + Q^T dP
+    const bool isq = part == 0;
+    f32x16 acc[3];
+    state_terms(isq ? Sdc : dSdc, isq ? sm.dO : sm.v, 32 * W, acc);
+    const float sc = isq ? sm.dec.lam[tl] : sm.dec.kap[tl];
+#pragma unroll
+    for (int db = 0; db < 3; ++db) acc[db] *= sc;
+    const bf16* xo = isq ? sm.k : sm.q;
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (isq ? (J > W) : (J < W)) continue;
+      const PairFrag D = isq ? dp_tile<true>(sm, J, W, tl, b_t) : dp_tile<false>(sm, J, W, tl, b_t);
+#pragma unroll
+      for (int db = 0; db < 3; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 ax = sfrag_kr(xo, 32 * J, 32 * db, s);
+          acc[db] = mfma(ax, D.hi[s], acc[db]);
+          acc[db] = mfma(ax, D.lo[s], acc[db]);
+        }
+    }
+    const bf16* xs = isq ? sm.q : sm.k;
+    TOut* out = (TOut*)(isq ? a.dq : a.dk) + tok * DK + 4 * g2;
+    float rr = 0.f;
 #pragma unroll
     for (int db = 0; db < 3; ++db) {
-      f32x16 aq = {};
-#pragma unroll
-      for (int kc = 0; kc < 12; ++kc) {
-        const bf16x8 bo = frag_kcN(sm.dO, PY, 32 * W, 32 * (kc >> 1), kc & 1);
-        aq = mfma(gfrag(Sdc, db * 12 + kc), bo, aq);
-        aq = mfma(gfrag(Sdc + DK * DV, db * 12 + kc), bo, aq);
-      }
-      aq *= lam;
-#pragma unroll
-      for (int J = 0; J <= W; ++J)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 ak = frag_kr(sm.k, PX, 32 * J, 32 * db, s);
-          aq = mfma(ak, D[J].hi[s], aq);
-          aq = mfma(ak, D[J].lo[s], aq);
-        }
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 qv = load4f(sm.q + tl * PX + 32 * db + 8 * qq + 4 * g2);
+        const bf16x4 xv = *(const LDS_AS bf16x4*)(to_lds(xs) + swz96(tl, 32 * db + 8 * qq + 4 * g2));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rq += qv[e] * aq[4 * qq + e];
+        for (int e = 0; e < 4; ++e) rr += (float)xv[e] * acc[db][4 * qq + e];
       }
       if (valid) {
-        TOut* pq = (TOut*)a.dq + tok * DK + 32 * db + 4 * g2;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
-          store4(pq + 8 * qq, f32x4{aq[4 * qq], aq[4 * qq + 1], aq[4 * qq + 2], aq[4 * qq + 3]});
+          store4(out + 32 * db + 8 * qq,
+                 f32x4{acc[db][4 * qq], acc[db][4 * qq + 1], acc[db][4 * qq + 2], acc[db][4 * qq + 3]});
       }
     }
+    r += isq ? rr : -rr;
   }
-
-  // ---- phase 3: dP (query rows i >= 32W, key column tl) and dK^T[:, W]
-  float rk = 0.f;
-  {
-    PairFrag D[4];
-#pragma unroll
-    for (int I = W; I < 4; ++I) {
-      f32x16 ad = {};
-#pragma unroll
-      for (int kb = 0; kb < 6; ++kb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          ad = mfma(frag_kcN(sm.dO, PY, 32 * I, 32 * kb, s), frag_kcN(sm.v, PY, 32 * W, 32 * kb, s), ad);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * I + out_row(r);
-        const float w = exp2f(fminf(sm.dec.b2[i] - b_t, 0.f));
-        ad[r] = ((I > W) || (tl <= i)) ? ad[r] * w : 0.f;
-      }
-      regs_to_frag_split(ad, 0, D[I].hi[0], D[I].lo[0]);
-      regs_to_frag_split(ad, 1, D[I].hi[1], D[I].lo[1]);
-    }
-#pragma unroll
-    for (int db = 0; db < 3; ++db) {
-      f32x16 ak = {};
-#pragma unroll
-      for (int kc = 0; kc < 12; ++kc) {
-        const bf16x8 bv = frag_kcN(sm.v, PY, 32 * W, 32 * (kc >> 1), kc & 1);
-        ak = mfma(gfrag(dSdc, db * 12 + kc), bv, ak);
-        ak = mfma(gfrag(dSdc + DK * DV, db * 12 + kc), bv, ak);
-      }
-      ak *= kap;
-#pragma unroll
-      for (int I = W; I < 4; ++I)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 aq = frag_kr(sm.q, PX, 32 * I, 32 * db, s);
-          ak = mfma(aq, D[I].hi[s], ak);
-          ak = mfma(aq, D[I].lo[s], ak);
-        }
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 kv = load4f(sm.k + tl * PX + 32 * db + 8 * qq + 4 * g2);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rk += kv[e] * ak[4 * qq + e];
-      }
-      if (valid) {
-        TOut* pk = (TOut*)a.dk + tok * DK + 32 * db + 4 * g2;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          store4(pk + 8 * qq, f32x4{ak[4 * qq], ak[4 * qq + 1], ak[4 * qq + 2], ak[4 * qq + 3]});
-      }
-    }
-  }
-  float r = rq - rk;
   r += __shfl_xor(r, 32, 64);
   if (lane < 32) sm.r[tl] = valid ? r : 0.f;
 }
 
+template <class TOut, int WV>
+__device__ __forceinline__ void bwd_wave(const BwdArgs& a, BwdSmem& sm, int64_t bh, int64_t b, int h, int n) {
+  constexpr int W = WV & 3;                        // token block
+  const int lane = lane_id();
+  const int64_t T = a.T;
+  const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
+  const bool valid = trow < T;
+  const int64_t tok = ((int64_t)b * T + trow) * a.H + h;
+  // per chunk: [hi fragments | lo fragments]
+  const int64_t frag_base = (bh * a.n_chunks + n) * (int64_t)(2 * DK * DV);
+  if constexpr (WV < 4)
+    bwd_dv_wave<TOut, W>(a, sm, (const bf16*)a.ds_cd + frag_base, tok, valid);
+  else
+    bwd_dqk_wave<TOut, W>(a, sm, (const bf16*)a.s_dc + frag_base, (const bf16*)a.ds_dc + frag_base, tok, valid);
+}
+
 template <class TOut>
-__global__ void __launch_bounds__(256, 1) bwd_chunk_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(512, 1) bwd_chunk_kernel(BwdArgs a) {
   __shared__ BwdSmem sm;
   const int N = a.n_chunks;
   const int64_t item = blockIdx.x;
@@ -253,10 +263,10 @@ __global__ void __launch_bounds__(256, 1) bwd_chunk_kernel(BwdArgs a) {
   const int64_t T = a.T;
   const int64_t t0 = (int64_t)n * CH;
   const int64_t rsx = (int64_t)a.H * DK, rsy = (int64_t)a.H * DV;
-  load_tile_lds(sm.q, BwdSmem::PX, (const bf16*)a.q + b * T * rsx + h * DK, rsx, DK, t0, T);
-  load_tile_lds(sm.k, BwdSmem::PX, (const bf16*)a.k + b * T * rsx + h * DK, rsx, DK, t0, T);
-  load_tile_lds(sm.v, BwdSmem::PY, (const bf16*)a.v + b * T * rsy + h * DV, rsy, DV, t0, T);
-  load_tile_lds(sm.dO, BwdSmem::PY, (const bf16*)a.dO + b * T * rsy + h * DV, rsy, DV, t0, T);
+  stage_tile<DK>(sm.q, (const bf16*)a.q + b * T * rsx + h * DK, rsx, t0, T);
+  stage_tile<DK>(sm.k, (const bf16*)a.k + b * T * rsx + h * DK, rsx, t0, T);
+  stage_tile<DV>(sm.v[0], (const bf16*)a.v + b * T * rsy + h * DV, rsy, t0, T);
+  stage_tile<DV>(sm.dO[0], (const bf16*)a.dO + b * T * rsy + h * DV, rsy, t0, T);
   if (threadIdx.x < 64) {
     const int l = threadIdx.x;
     const float* gb = a.g + b * T * a.H + h;
@@ -269,7 +279,11 @@ __global__ void __launch_bounds__(256, 1) bwd_chunk_kernel(BwdArgs a) {
     case 0: bwd_wave<TOut, 0>(a, sm, bh, b, h, n); break;
     case 1: bwd_wave<TOut, 1>(a, sm, bh, b, h, n); break;
     case 2: bwd_wave<TOut, 2>(a, sm, bh, b, h, n); break;
-    default: bwd_wave<TOut, 3>(a, sm, bh, b, h, n); break;
+    case 3: bwd_wave<TOut, 3>(a, sm, bh, b, h, n); break;
+    case 4: bwd_wave<TOut, 4>(a, sm, bh, b, h, n); break;
+    case 5: bwd_wave<TOut, 5>(a, sm, bh, b, h, n); break;
+    case 6: bwd_wave<TOut, 6>(a, sm, bh, b, h, n); break;
+    default: bwd_wave<TOut, 7>(a, sm, bh, b, h, n); break;
   }
   __syncthreads();
   if (threadIdx.x < 64) {
@@ -322,7 +336,7 @@ __global__ void __launch_bounds__(256) dg_finish_kernel(float* dg, const float* 
 }
 
 hipError_t launch_bwd_chunks(const BwdArgs& a, int out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)(a.B * a.H * a.n_chunks)), block(256);
+  const dim3 grid((unsigned)(a.B * a.H * a.n_chunks)), block(512);
   if (out_bf16) hipLaunchKernelGGL((bwd_chunk_kernel<bf16>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((bwd_chunk_kernel<float>), grid, block, 0, st, a);
   return hipGetLastError();
