@@ -23,8 +23,10 @@
 // With bf16 inputs the inputs themselves are exact MFMA operands, but the
 // intermediates (decay-masked scores, the bf16 copy of the fp32 state, the
 // decay-weighted keys) are not: each is split into a bf16 value and its bf16
-// residual and multiplied as two MFMAs (error-compensated 16-bit products, as
-// the HEAL page "Problema" / "HEAL-B" sections describe for bf16 inference).
+// residual and multiplied as two MFMAs (the error-compensated 16-bit products
+// of section "B. Mitigando o Truncamento de GEMM via Compensação de Erro
+// Algébrica" on the page "Resumo Técnico: Desmistificando a Instabilidade
+// Numérica na Inferência de LLMs com HEAL").
 #include <type_traits>
 
 #include "gla_common.h"
@@ -81,15 +83,17 @@ struct WalkSmem {
   TIn xh[COMP ? CH * PX : 8];             // decay-weighted keys: bf16 value ...
   TIn xl[COMP ? CH * PX : 8];             // ... and bf16 residual
   TIn y[CH * PY];                         // values (reverse walk: dO), this dv-slice
-  TIn q[(OUT && !COMP) ? CH * PQ : 8];    // queries (fp32 inputs only; bf16 queries stay in registers)
+  TIn q[OUT ? CH * PQ : 8];               // queries
   TIn z[DK * PZ];                         // state entering the chunk, [d][c]
   TIn zl[COMP ? DK * PZ : 8];             // residual of its bf16 copy
-  // Decay tables of the chunk being processed and of the next one (built a
-  // chunk ahead so the weighted keys can be written before the main barrier).
-  DecayLds dec[2];
+  // Decay tables: the other walks keep the current chunk's and the next
+  // one's (built a chunk ahead); the bf16 prefill rebuilds one set in the
+  // phase where nobody reads it.
+  static constexpr int NDEC = (OUT && COMP) ? 1 : 2;
+  DecayLds dec[NDEC];
   // utab[U(I) + j] = 2^{b_{32I} - b_j} for j < 32I (I = 1, 2, 3; U = 0, 32, 96):
   // the key-side factor of the decay between token blocks.
-  float utab[2][OUT ? 192 : 4];
+  float utab[NDEC][OUT ? 192 : 4];
 };
 
 __device__ __forceinline__ int utab_off(int I) { return I == 1 ? 0 : I == 2 ? 32 : 96; }
@@ -104,17 +108,17 @@ struct TileRegs {
   static constexpr int NP = CH * PPR;
   static constexpr int PER = (NP + NTHR - 1) / NTHR;
   uint4 r[PER];
+  __device__ __forceinline__ void load_piece(int i, const T* base, int64_t row_stride, int t0, int64_t T_len) {
+    const int p = (threadIdx.x & (NTHR - 1)) + NTHR * i;
+    const int row = p / PPR, cp = p % PPR;
+    if (p < NP && t0 + row < T_len)
+      r[i] = *(const uint4*)(base + (int64_t)(t0 + row) * row_stride + cp * EPP);
+    else
+      r[i] = make_uint4(0, 0, 0, 0);
+  }
   __device__ __forceinline__ void load(const T* base, int64_t row_stride, int t0, int64_t T_len) {
-    const int tid = threadIdx.x & (NTHR - 1);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int p = tid + NTHR * i;
-      const int row = p / PPR, cp = p % PPR;
-      if (p < NP && t0 + row < T_len)
-        r[i] = *(const uint4*)(base + (int64_t)(t0 + row) * row_stride + cp * EPP);
-      else
-        r[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < PER; ++i) load_piece(i, base, row_stride, t0, T_len);
   }
   template <int PITCH>
   __device__ __forceinline__ void store(T* lds) const {
@@ -132,10 +136,12 @@ struct TileRegs {
   // bf16 rows scaled by w[row], stored as compensated hi/lo copies.
   template <int PITCH>
   __device__ __forceinline__ void store_weighted(bf16* hi, bf16* lo, const float* w) const {
-    const int tid = threadIdx.x & (NTHR - 1);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int p = tid + NTHR * i;
+    for (int i = 0; i < PER; ++i) store_weighted_piece(i, hi, lo, w);
+  }
+  __device__ __forceinline__ void store_weighted_piece(int i, bf16* hi, bf16* lo, const float* w) const {
+    {
+      const int p = (threadIdx.x & (NTHR - 1)) + NTHR * i;
       if (p < NP) {
         const int row = p / PPR, cp = p % PPR;
         const float s = w[row];
@@ -573,6 +579,352 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     a.seg_decay[bh * a.seg_decay_bh_stride + gseg] = decay_sum;
 }
 
+// bf16 prefill with output: 8 waves.  For chunk n (decay tables dec[n&1]):
+//   phase 1  output waves: stage their own 32 query rows, decay-masked scores
+//                          P from the queries and keys, and
+//                          O = diag(Lambda) (Q S_n) from the published bf16
+//                          value/residual copy of S_n
+//            state waves:  stage the values and the decay-weighted keys of
+//                          chunk n and request chunk n+1's values and keys
+//   barrier
+//   phase 2  output waves: O += P V, request their queries of chunk n+1,
+//                          store O; wave 0 builds the decay tables of n+1
+//            state waves:  S_n+1 = Gamma S_n + (diag(kappa) K)^T V, publish
+//                          S_n+1, stage the keys of chunk n+1
+//   barrier
+// Every LDS tile (and the decay tables) is read in one phase only and
+// rewritten in the other, so one buffer of each suffices and the staging
+// overlaps the products.  All tiles are read from memory with row-contiguous
+// 16-byte accesses, spread over both phases so that the workgroups on the
+// chip keep the memory busy instead of all loading at the same moment.
+template <class TOut, int W>
+__device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3, true>& sm, int b, int h,
+                                             int slice, int seg) {
+  using S = WalkSmem<bf16, 3, true>;
+  constexpr int NC = 3;
+  constexpr int DVS = 96;
+  constexpr bool OUTW = W < 4;                        // output wave (else: state wave)
+  constexpr int U = OUTW ? 0 : W - 4;                 // index among the state waves
+  constexpr int NT = OUTW ? 0 : Own<NC, true>::count(U);
+  constexpr int T0 = OUTW ? 0 : Own<NC, true>::first(U);
+  constexpr int NTHR = 256;                           // loader threads: the 4 state waves
+
+  const int lane = lane_id();
+  const int g2 = lane >> 5;
+  const int c0 = slice * DVS;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t T = a.T;
+  const bf16* Xb = (const bf16*)a.X + (int64_t)b * T * a.H * DK + (int64_t)h * DK;
+  const bf16* Yb = (const bf16*)a.Y + (int64_t)b * T * a.H * DV + (int64_t)h * DV + c0;
+  const bf16* Qb = (const bf16*)a.Q + (int64_t)b * T * a.H * DK + (int64_t)h * DK;
+  const float* gb = a.g + (int64_t)b * T * a.H + h;
+  const int gseg = seg + a.seg_offset;
+  const int n_begin = gseg * a.cps;
+  const int n_end = min(a.n_chunks, n_begin + a.cps);
+  const int nloc = n_end - n_begin;
+
+  // ---- state tiles Z^T (c rows, d columns): initial state or zero
+  f32x16 z[NT > 0 ? NT : 1];
+  {
+    const float* zi = a.zinit ? a.zinit + bh * a.zinit_bh_stride + (int64_t)gseg * a.zinit_seg_stride : nullptr;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
+      const int d = 32 * db + (lane & 31);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        f32x4 v = zi ? load4f(zi + (int64_t)d * DV + c0 + 32 * cb + 8 * qq + 4 * g2) : f32x4{0, 0, 0, 0};
+        z[t][4 * qq + 0] = v[0]; z[t][4 * qq + 1] = v[1];
+        z[t][4 * qq + 2] = v[2]; z[t][4 * qq + 3] = v[3];
+      }
+    }
+  }
+
+  TileRegs<bf16, DK, NTHR> px;                          // keys of the chunk being staged
+  TileRegs<bf16, DVS, NTHR> py;                         // and its values
+  // an output wave's 32 query rows: 12 pieces of 16 bytes per row, 6 per lane
+  uint4 qr[OUTW ? 6 : 1];
+  auto load_q = [&](int n) {
+    if constexpr (OUTW) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int p = lane + 64 * i, row = p / 12, cp = p % 12;
+        const int64_t t = (int64_t)n * CH + 32 * W + row;
+        qr[i] = t < T ? *(const uint4*)(Qb + t * a.H * DK + cp * 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stage_q = [&]() {
+    if constexpr (OUTW) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int p = lane + 64 * i, row = p / 12, cp = p % 12;
+        *(uint4*)(sm.q + swz96(32 * W + row, cp * 8)) = qr[i];
+      }
+    }
+  };
+  // publish the state as a bf16 value/residual pair
+  auto publish = [&]() {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
+      const int d = 32 * db + (lane & 31);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int off = swz96(d, 32 * cb + 8 * qq + 4 * g2);
+        store4_split((bf16*)sm.z + off, (bf16*)sm.zl + off,
+                     f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]});
+      }
+    }
+  };
+  // log-decay of chunk n for wave 0: tokens 2l, 2l+1 and the mirrored
+  // 127-2l, 126-2l; zero past T
+  float gx0 = 0.f, gx1 = 0.f, gm0 = 0.f, gm1 = 0.f;
+  auto load_g = [&](int n) {
+    if (W == 0) {
+      const int64_t t0 = (int64_t)n * CH;
+      const int64_t ta = t0 + 2 * lane, tb = ta + 1, tc = t0 + 127 - 2 * lane, td = tc - 1;
+      gx0 = ta < T ? gb[ta * a.H] : 0.f;
+      gx1 = tb < T ? gb[tb * a.H] : 0.f;
+      gm0 = tc < T ? gb[tc * a.H] : 0.f;
+      gm1 = td < T ? gb[td * a.H] : 0.f;
+    }
+  };
+
+  if (nloc > 0) {
+    if constexpr (!OUTW) {
+      px.load(Xb, (int64_t)a.H * DK, n_begin * CH, T);
+      py.load(Yb, (int64_t)a.H * DV, n_begin * CH, T);
+    }
+    load_q(n_begin);
+    load_g(n_begin);
+    if (W == 0) build_decay(&sm.dec[0], gx0, gx1, gm0, gm1, sm.utab[0]);
+    if (nloc > 1) load_g(n_begin + 1);
+    publish();
+    if constexpr (!OUTW) px.template store<S::PX>(sm.x);
+  }
+  __syncthreads();
+
+  float decay_sum = 0.f;
+  for (int it = 0; it < nloc; ++it) {
+    const int n = n_begin + it;
+    const DecayLds& dc = sm.dec[0];
+    decay_sum += dc.blast;
+
+    // ================= phase 1
+    f32x16 o[NC];
+    bf16x8 pf[OUTW ? W + 1 : 1][2], pl[OUTW ? W + 1 : 1][2];
+    float gam = 0.f;
+    if constexpr (OUTW) {
+      const int il = 32 * W + (lane & 31);            // this lane's token inside the chunk
+      const float bi = dc.b2[il];
+      // this wave's 32 queries as plain-order MFMA B operands (the wave reads
+      // back only the rows it wrote itself)
+      stage_q();
+      bf16x8 qcur[3][2];
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) qcur[kb][s] = sfrag_kcN(sm.q, 32 * W, 32 * kb, s);
+      // O^T = diag(Lambda) (Z^T Q^T), operands of step k+1 requested before
+      // the products of step k
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) o[cb] = f32x16{};
+      bf16x8 zh[2][NC], zlo[2][NC];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        zh[0][cb] = sfrag_krN((const bf16*)sm.z, 0, 32 * cb, 0);
+        zlo[0][cb] = sfrag_krN((const bf16*)sm.zl, 0, 32 * cb, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const int bf = k & 1, kb = k >> 1, s = k & 1;
+        if (k + 1 < 6) {
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb) {
+            zh[bf ^ 1][cb] = sfrag_krN((const bf16*)sm.z, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
+            zlo[bf ^ 1][cb] = sfrag_krN((const bf16*)sm.zl, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
+          }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+          o[cb] = mfma(zh[bf][cb], qcur[kb][s], o[cb]);
+          o[cb] = mfma(zlo[bf][cb], qcur[kb][s], o[cb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one step of operands in flight
+      }
+      const float lam = dc.lam[il];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) o[cb] *= lam;
+      // Decay-masked scores P^T (keys j in rows, queries i in columns).  Off
+      // the diagonal 2^{b_i - b_j} = 2^{b_i - b_{32W}} 2^{b_{32W} - b_j}.
+      f32x16 acc[W + 1];
+#pragma unroll
+      for (int J = 0; J <= W; ++J) acc[J] = f32x16{};
+      {
+        bf16x8 xk[2][W + 1];
+#pragma unroll
+        for (int J = 0; J <= W; ++J) xk[0][J] = sfrag_kcN(sm.x, 32 * J, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          const int bf = k & 1, kb = k >> 1, s = k & 1;
+          if (k + 1 < 6) {
+#pragma unroll
+            for (int J = 0; J <= W; ++J) xk[bf ^ 1][J] = sfrag_kcN(sm.x, 32 * J, 32 * ((k + 1) >> 1), (k + 1) & 1);
+          }
+#pragma unroll
+          for (int J = 0; J <= W; ++J) acc[J] = mfma(xk[bf][J], qcur[kb][s], acc[J]);
+          __builtin_amdgcn_sched_barrier(0);   // one step of operands in flight
+        }
+      }
+      const float ri = W > 0 ? exp2f(bi - dc.b2[32 * W]) : 1.f;
+#pragma unroll
+      for (int J = 0; J <= W; ++J) {
+        if (J < W) {
+          const float* u = sm.utab[0] + utab_off(W) + 32 * J + 4 * g2;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 uu = *(const f32x4*)(u + 8 * qq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[J][4 * qq + e] *= uu[e] * ri;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * J + out_row(r);
+            const float w = exp2f(fminf(bi - dc.b2[j], 0.f));
+            acc[J][r] = j <= il ? acc[J][r] * w : 0.f;
+          }
+        }
+        split_tile(acc[J], 0, pf[J][0], pl[J][0]);
+        split_tile(acc[J], 1, pf[J][1], pl[J][1]);
+      }
+    } else {
+      gam = dc.gam;
+      py.template store<S::PY>(sm.y);
+      if (it + 1 < nloc) py.load(Yb, (int64_t)a.H * DV, (n + 1) * CH, T);
+#pragma unroll
+      for (int i = 0; i < decltype(px)::PER; ++i) {
+        px.store_weighted_piece(i, (bf16*)sm.xh, (bf16*)sm.xl, dc.kap);
+        if (it + 1 < nloc) px.load_piece(i, Xb, (int64_t)a.H * DK, (n + 1) * CH, T);
+      }
+    }
+    __syncthreads();                                   // weighted keys and values visible; queries, keys, state copy and tables read
+
+    // ================= phase 2
+    if constexpr (OUTW) {
+      // O^T += V^T P^T
+      constexpr int NK = 2 * (W + 1);                   // (J, s) steps
+      bf16x8 yv[2][NC];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) yv[0][cb] = sfrag_kr(sm.y, 0, 32 * cb, 0);
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int bf = k & 1, J = k >> 1, s = k & 1;
+        if (k + 1 < NK) {
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb) yv[bf ^ 1][cb] = sfrag_kr(sm.y, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+          o[cb] = mfma(yv[bf][cb], pf[J][s], o[cb]);
+          o[cb] = mfma(yv[bf][cb], pl[J][s], o[cb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one step of operands in flight
+      }
+      if constexpr (std::is_same<TOut, bf16>::value) {
+        // Through this wave's own rows of the query tile (free until the
+        // next phase 1): written in the accumulator layout, read back and
+        // stored as row-contiguous 16-byte pieces.
+        bf16* ot = sm.q + 32 * W * 96;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            store4(ot + swz96(lane & 31, 32 * cb + 8 * qq + 4 * g2),
+                   f32x4{o[cb][4 * qq], o[cb][4 * qq + 1], o[cb][4 * qq + 2], o[cb][4 * qq + 3]});
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          const int p = lane + 64 * i, row = p / 12, cp = p % 12;
+          const uint4 v = *(const uint4*)(ot + swz96(row, cp * 8));
+          const int64_t t = (int64_t)n * CH + 32 * W + row;
+          if (t < T) *(uint4*)((bf16*)a.O + (((int64_t)b * T + t) * a.H + h) * DV + c0 + cp * 8) = v;
+        }
+      } else {
+        const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
+        if (trow < T) {
+          TOut* op = (TOut*)a.O + (((int64_t)b * T + trow) * a.H + h) * DV + c0 + 4 * g2;
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+              store4(op + 32 * cb + 8 * qq,
+                     f32x4{o[cb][4 * qq], o[cb][4 * qq + 1], o[cb][4 * qq + 2], o[cb][4 * qq + 3]});
+        }
+      }
+      // the next chunk's query loads (24 registers) after the products and stores
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + 1 < nloc) load_q(n + 1);
+      if (W == 0 && it + 1 < nloc) {
+        build_decay(&sm.dec[0], gx0, gx1, gm0, gm1, sm.utab[0]);
+        if (it + 2 < nloc) load_g(n + 2);
+      }
+    } else {
+      // Z^T = Gamma Z^T + V^T (kappa K), over the 8 (token block, half) steps
+#pragma unroll
+      for (int t = 0; t < NT; ++t) z[t] *= gam;
+      constexpr int DB_LO = (NT >= 3) ? 0 : (T0 % 3);
+      constexpr int DB_N = (NT >= 3) ? 3 : NT;        // contiguous db range (mod 3) when NT < 3
+      constexpr int CB_LO = T0 / 3, NCB = (T0 + NT - 1) / 3 - CB_LO + 1;
+      bf16x8 bx[2][3], bl[2][3], ay[2][NCB];
+      auto load_ops = [&](int buf, int k) {
+        const int J = k >> 1, s = k & 1;
+#pragma unroll
+        for (int q = 0; q < DB_N; ++q) {
+          const int db = (DB_LO + q) % 3;
+          bx[buf][db] = sfrag_kr((const bf16*)sm.xh, 32 * J, 32 * db, s);
+          bl[buf][db] = sfrag_kr((const bf16*)sm.xl, 32 * J, 32 * db, s);
+        }
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) ay[buf][c] = sfrag_kr(sm.y, 32 * J, 32 * (CB_LO + c), s);
+      };
+      load_ops(0, 0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int bf = k & 1;
+        if (k + 1 < 8) load_ops(bf ^ 1, k + 1);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
+          z[t] = mfma(ay[bf][cb - CB_LO], bx[bf][db], z[t]);
+          z[t] = mfma(ay[bf][cb - CB_LO], bl[bf][db], z[t]);
+        }
+      }
+      if (it + 1 < nloc) {
+        publish();
+        px.template store<S::PX>(sm.x);
+      }
+    }
+    __syncthreads();                                   // next chunk's keys, tables and state copy visible
+  }
+
+  // ---- final state
+  if (a.zfin && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
+    float* zo = a.zfin + bh * a.zfin_bh_stride + (int64_t)gseg * a.zfin_seg_stride;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
+      const int d = 32 * db + (lane & 31);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        store4(zo + (int64_t)d * DV + c0 + 32 * cb + 8 * qq + 4 * g2,
+               f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]});
+    }
+  }
+  if (a.seg_decay && slice == 0 && threadIdx.x == 0)
+    a.seg_decay[bh * a.seg_decay_bh_stride + gseg] = decay_sum;
+}
+
 template <class TIn, class TOut, int NC, int MODE>
 __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkArgs a) {
   __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
@@ -589,6 +941,19 @@ __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkA
   rest /= a.nseg_launch;
   const int h = rest % a.H;
   const int b = rest / a.H;
+  if constexpr (MODE == WALK_FWD_OUT && std::is_same<TIn, bf16>::value) {
+    switch (threadIdx.x >> 6) {
+      case 0: prefill_wave<TOut, 0>(a, sm, b, h, slice, seg); break;
+      case 1: prefill_wave<TOut, 1>(a, sm, b, h, slice, seg); break;
+      case 2: prefill_wave<TOut, 2>(a, sm, b, h, slice, seg); break;
+      case 3: prefill_wave<TOut, 3>(a, sm, b, h, slice, seg); break;
+      case 4: prefill_wave<TOut, 4>(a, sm, b, h, slice, seg); break;
+      case 5: prefill_wave<TOut, 5>(a, sm, b, h, slice, seg); break;
+      case 6: prefill_wave<TOut, 6>(a, sm, b, h, slice, seg); break;
+      default: prefill_wave<TOut, 7>(a, sm, b, h, slice, seg); break;
+    }
+    return;
+  } else {
   switch (threadIdx.x >> 6) {
     case 0: walk_wave<TIn, TOut, NC, MODE, 0>(a, sm, b, h, slice, seg); break;
     case 1: walk_wave<TIn, TOut, NC, MODE, 1>(a, sm, b, h, slice, seg); break;
@@ -604,6 +969,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkA
         }
       }
       break;
+  }
   }
 }
 
