@@ -125,93 +125,106 @@ FwdPlan plan_fwd(const gla_dims* d) {
   return p;
 }
 
-// Runs the state walk of one direction over all chunks, with segment-parallel
-// passes when nseg > 1: pass 1 (state change of each segment from zero, all
-// but the segment that ends the walk), a scan over segments, then the full
-// walk of every segment from its entering state.
-hipError_t run_walk(WalkArgs base, int variant, int ns, int nseg, int cps, int n_chunks, bool rev,
-                    const float* Z0, float* Zfin, float* seg_states, float* seg_decay, int64_t BH,
-                    hipStream_t st) {
-  base.ns = ns;
-  base.n_chunks = n_chunks;
-  base.cps = cps;
-  if (nseg == 1) {
-    base.zinit = Z0;
-    base.zinit_bh_stride = kStateElems;
-    base.zinit_seg_stride = 0;
-    base.zfin = Zfin;
-    base.zfin_bh_stride = kStateElems;
-    base.zfin_seg_stride = 0;
-    base.zfin_only_seg = -1;
-    base.seg_decay = nullptr;
-    base.nseg_launch = 1;
-    base.seg_offset = 0;
-    return launch_walk(base, variant, (int)(BH * ns), st);
-  }
-  // pass 1: state change per segment, without outputs or per-chunk exports
-  WalkArgs p1 = base;
-  const int state_variant = (variant == WV_REV_BF16) ? WV_REV_BF16
-                            : (variant == WV_FWD_OUT_F32_F32 || variant == WV_FWD_OUT_F32_BF16 ||
-                               variant == WV_FWD_STATE_F32)
-                                ? WV_FWD_STATE_F32
-                                : WV_FWD_STATE_BF16;
-  p1.Q = nullptr;
-  p1.O = nullptr;
-  p1.st_dc = p1.st_cd = nullptr;
-  p1.zinit = nullptr;
-  p1.zfin = seg_states;
-  p1.zfin_bh_stride = (int64_t)nseg * kStateElems;
-  p1.zfin_seg_stride = kStateElems;
-  p1.zfin_only_seg = -1;
-  p1.seg_decay = seg_decay;
-  p1.seg_decay_bh_stride = nseg;
-  p1.nseg_launch = nseg - 1;
-  p1.seg_offset = rev ? 1 : 0;
-  hipError_t e = launch_walk(p1, state_variant, (int)(BH * ns * (nseg - 1)), st);
-  if (e != hipSuccess) return e;
-  e = launch_seg_scan(seg_states, seg_decay, Z0, BH, nseg, rev ? 1 : 0, st);
-  if (e != hipSuccess) return e;
-  WalkArgs p2 = base;
-  p2.zinit = seg_states;
-  p2.zinit_bh_stride = (int64_t)nseg * kStateElems;
-  p2.zinit_seg_stride = kStateElems;
-  p2.zfin = Zfin;
-  p2.zfin_bh_stride = kStateElems;
-  p2.zfin_seg_stride = 0;
-  p2.zfin_only_seg = rev ? 0 : nseg - 1;
-  p2.seg_decay = nullptr;
-  p2.nseg_launch = nseg;
-  p2.seg_offset = 0;
-  return launch_walk(p2, variant, (int)(BH * ns * nseg), st);
+// A [B,T,H,cols] row-major tensor of `esize`-byte elements, read forwards or
+// backwards in time, in dv-slices of `slice_w` columns.
+TokView tok_view(const void* p, size_t esize, const gla_dims* d, int cols, int slice_w, bool backwards) {
+  TokView v;
+  const int64_t row = (int64_t)d->H * cols;
+  v.sb = d->T * row;
+  v.sh = cols;
+  v.ss = slice_w;
+  v.st = backwards ? -row : row;
+  v.p = backwards ? (const void*)((const char*)p + (d->T - 1) * row * (int64_t)esize) : p;
+  return v;
 }
 
+// [BH][DK][DV] fp32 states.  A walk's state element (x index i, y index j) of
+// slice s is S[i][s*w + j] when the walk's keys span dk (plain), or
+// S[j][s*w + i] when its keys span a dv-slice (transposed).
+StateView state_plain(float* p, int w) { return StateView{p, kStateElems, 0, w, DV, 1}; }
+StateView state_transposed(float* p, int w) { return StateView{p, kStateElems, 0, w, 1, DV}; }
+
+// The same layout for the per-segment states [BH][nseg][DK][DV].
+StateView seg_view(float* p, StateView lay, int nseg) {
+  lay.p = p;
+  lay.sbh = (int64_t)nseg * kStateElems;
+  lay.sseg = kStateElems;
+  return lay;
+}
+
+struct SegPlan {
+  int ns, nseg, cps, n_chunks;
+};
+
+void set_plan(WalkArgs& a, const SegPlan& sp) {
+  a.ns = sp.ns;
+  a.n_chunks = sp.n_chunks;
+  a.cps = sp.cps;
+}
+
+// Segment pass 1 and scan: the state change of every segment but the last
+// from a zero state, then a scan over segments from z0, which leaves in
+// `seg` the state entering every segment.  z0 and seg share one layout.
+hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, const float* z0, StateView seg,
+                          float* seg_decay, int64_t BH, hipStream_t st) {
+  set_plan(a, sp);
+  a.zinit = StateView{};
+  a.zfin = seg;
+  a.zfin_only_seg = -1;
+  a.seg_decay = seg_decay;
+  a.seg_decay_bh_stride = sp.nseg;
+  a.nseg_launch = sp.nseg - 1;
+  a.seg_offset = 0;
+  hipError_t e = launch_walk(a, state_variant, (int)(BH * sp.ns * (sp.nseg - 1)), st);
+  if (e != hipSuccess) return e;
+  return launch_seg_scan(seg.p, seg_decay, z0, BH, sp.nseg, 0, st);
+}
+
+// The walk of every segment from its entering state (zinit: the segment
+// states, or the initial state when there is one segment); the final state
+// comes from the last segment.
+hipError_t walk_segments(WalkArgs a, int variant, const SegPlan& sp, StateView zinit, StateView zfin, int64_t BH,
+                         hipStream_t st) {
+  set_plan(a, sp);
+  a.zinit = zinit;
+  a.zfin = zfin;
+  a.zfin.sseg = 0;
+  a.zfin_only_seg = sp.nseg > 1 ? sp.nseg - 1 : -1;
+  a.seg_decay = nullptr;
+  a.nseg_launch = sp.nseg;
+  a.seg_offset = 0;
+  return launch_walk(a, variant, (int)(BH * sp.ns * sp.nseg), st);
+}
+
+// Backward workspace: fp32 partial sums of dq and dk over the two dv-halves
+// ([2][B,T,H,DK] each), the final forward state, per-chunk sums of the
+// log-decay gradient, and the segment states and decays of the forward and
+// the backward-in-time recurrences.
 struct BwdPlan {
-  int n_chunks, nseg_f, cps_f, nseg_r, cps_r, ns;
-  size_t off_s, off_dsdc, off_dscd, off_st, off_r, off_seg, off_dec, ws_total;
+  SegPlan sp;
+  size_t off_dq, off_dk, off_st, off_r, off_segf, off_segr, off_decf, off_decr, ws_total;
 };
 
 BwdPlan plan_bwd(const gla_dims* d) {
   BwdPlan p{};
-  p.n_chunks = (int)((d->T + CH - 1) / CH);
-  p.ns = walk_slices(WV_REV_BF16);
+  p.sp.n_chunks = (int)((d->T + CH - 1) / CH);
+  p.sp.ns = DV / 96;
   const int64_t BH = d->B * d->H;
-  const int64_t walkers = BH * p.ns;
-  p.nseg_f = plan_segments(walkers, p.n_chunks, "GLA_BWD_SEGMENTS");
-  p.cps_f = (p.n_chunks + p.nseg_f - 1) / p.nseg_f;
-  p.nseg_f = (p.n_chunks + p.cps_f - 1) / p.cps_f;
-  p.nseg_r = p.nseg_f;
-  p.cps_r = p.cps_f;
-  const size_t frag = (size_t)BH * p.n_chunks * kStateElems * 2 * 2;   // bf16 hi + lo fragments
+  p.sp.nseg = plan_segments(BH * p.sp.ns, p.sp.n_chunks, "GLA_BWD_SEGMENTS");
+  p.sp.cps = (p.sp.n_chunks + p.sp.nseg - 1) / p.sp.nseg;
+  p.sp.nseg = (p.sp.n_chunks + p.sp.cps - 1) / p.sp.cps;
+  const size_t part = align256((size_t)2 * d->B * d->T * d->H * DK * sizeof(float));
   size_t off = 0;
-  p.off_s = off; off += align256(frag);
-  p.off_dsdc = off; off += align256(frag);
-  p.off_dscd = off; off += align256(frag);
+  p.off_dq = off; off += part;
+  p.off_dk = off; off += part;
   p.off_st = off; off += align256((size_t)BH * kStateElems * sizeof(float));
-  p.off_r = off; off += align256((size_t)BH * p.n_chunks * sizeof(float));
-  p.off_seg = off;
-  if (p.nseg_f > 1) off += align256((size_t)BH * p.nseg_f * kStateElems * sizeof(float));
-  p.off_dec = off;
-  if (p.nseg_f > 1) off += align256((size_t)BH * p.nseg_f * sizeof(float));
+  p.off_r = off; off += align256((size_t)BH * p.sp.n_chunks * sizeof(float));
+  const size_t seg = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.nseg * kStateElems * sizeof(float)) : 0;
+  const size_t dec = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.nseg * sizeof(float)) : 0;
+  p.off_segf = off; off += seg;
+  p.off_segr = off; off += seg;
+  p.off_decf = off; off += dec;
+  p.off_decr = off; off += dec;
   p.ws_total = off;
   return p;
 }
@@ -313,20 +326,34 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, con
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  const size_t isz = dims->in_dtype == GLA_BF16 ? 2 : 4, osz = dims->out_dtype == GLA_BF16 ? 2 : 4;
+  const int w = DV / p.ns;                        // dv-slice width
   WalkArgs a{};
-  a.X = k;
-  a.Y = v;
-  a.Q = q;
+  a.X = tok_view(k, isz, dims, DK, 0, false);
+  a.Y = tok_view(v, isz, dims, DV, w, false);
+  a.Q = tok_view(q, isz, dims, DK, 0, false);
+  a.O = tok_view(o, osz, dims, DV, w, false);
   a.g = g;
-  a.O = o;
+  a.gsb = dims->T * dims->H;
+  a.gsh = 1;
+  a.gst = dims->H;
   a.B = dims->B;
   a.T = dims->T;
   a.H = dims->H;
-  char* w = (char*)ws;
-  float* seg_states = p.nseg > 1 ? (float*)w : nullptr;
-  float* seg_decay = p.nseg > 1 ? (float*)(w + p.ws_seg_states) : nullptr;
-  hipError_t e = run_walk(a, p.variant, p.ns, p.nseg, p.cps, p.n_chunks, false, S0, S_T, seg_states, seg_decay,
-                          dims->B * dims->H, (hipStream_t)stream);
+  const int64_t BH = dims->B * dims->H;
+  const SegPlan sp{p.ns, p.nseg, p.cps, p.n_chunks};
+  const StateView z0 = state_plain(const_cast<float*>(S0), w), zfin = state_plain(S_T, w);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (p.nseg > 1) {
+    char* wsb = (char*)ws;
+    const StateView seg = seg_view((float*)wsb, z0, p.nseg);
+    const int state_variant = dims->in_dtype == GLA_BF16 ? WV_FWD_STATE_BF16 : WV_FWD_STATE_F32;
+    e = segment_states(a, state_variant, sp, S0, seg, (float*)(wsb + p.ws_seg_states), BH, st);
+    if (e == hipSuccess) e = walk_segments(a, p.variant, sp, seg, zfin, BH, st);
+  } else {
+    e = walk_segments(a, p.variant, sp, z0, zfin, BH, st);
+  }
   return device_err(e, "gla_chunk_fwd launch");
 }
 
@@ -376,51 +403,114 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   const BwdPlan p = plan_bwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   TRY(check_ptr(ws, "ws", false));
-  if (p.n_chunks > 1024) return fail(GLA_ERR_UNSUPPORTED, "the backward supports at most 1024 chunks (T <= 131072)");
+  if (p.sp.n_chunks > 1024) return fail(GLA_ERR_UNSUPPORTED, "the backward supports at most 1024 chunks (T <= 131072)");
   char* w = (char*)ws;
   const int64_t BH = dims->B * dims->H;
+  const SegPlan& sp = p.sp;
+  const int hw = 96;                              // dv-half width
+  const size_t osz = dims->out_dtype == GLA_BF16 ? 2 : 4;
+  const int out_variant = dims->out_dtype == GLA_BF16 ? WV_FWD_OUT_BF16_BF16 : WV_FWD_OUT_BF16_F32;
   hipStream_t st = (hipStream_t)stream;
-  float* seg_states = p.nseg_f > 1 ? (float*)(w + p.off_seg) : nullptr;
-  float* seg_decay = p.nseg_f > 1 ? (float*)(w + p.off_dec) : nullptr;
+  float* dq_part = (float*)(w + p.off_dq);
+  float* dk_part = (float*)(w + p.off_dk);
   float* S_T = (float*)(w + p.off_st);
+  float* seg_f = sp.nseg > 1 ? (float*)(w + p.off_segf) : nullptr;
+  float* seg_r = sp.nseg > 1 ? (float*)(w + p.off_segr) : nullptr;
+  const int64_t plane = dims->B * dims->T * dims->H * DK;   // between the two partial sums
+  // fp32 partial-sum outputs [2][B,T,H,DK], one plane per dv-half
+  auto part_view = [&](float* base, bool backwards) {
+    TokView v = tok_view(base, 4, dims, DK, 0, backwards);
+    v.ss = plane;
+    return v;
+  };
 
-  // 1. forward states entering every chunk (and S_T when dS_T is given)
+  // 1. dq.  Forward recurrence with keys = a dv-half of v, values = k (its
+  //    state is the half of S^T), queries = the same half of dO; the two
+  //    halves give partial sums of dq.  Also S_T when dS_T is given.
   WalkArgs f{};
-  f.X = k;
-  f.Y = v;
+  f.X = tok_view(v, 2, dims, DV, hw, false);
+  f.Y = tok_view(k, 2, dims, DK, 0, false);
+  f.Q = tok_view(dO, 2, dims, DV, hw, false);
+  f.O = part_view(dq_part, false);
   f.g = g;
+  f.gsb = dims->T * dims->H;
+  f.gsh = 1;
+  f.gst = dims->H;
   f.B = dims->B;
   f.T = dims->T;
   f.H = dims->H;
-  f.st_dc = w + p.off_s;
-  hipError_t e = run_walk(f, WV_FWD_STATE_BF16, p.ns, p.nseg_f, p.cps_f, p.n_chunks, false, S0,
-                          dS_T ? S_T : nullptr, seg_states, seg_decay, BH, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd forward-state walk");
-  // 2. state gradients leaving every chunk (and dS0)
+  const StateView f0 = state_transposed(const_cast<float*>(S0), hw);
+  const StateView ffin = state_transposed(dS_T ? S_T : nullptr, hw);
+  hipError_t e = hipSuccess;
+  if (sp.nseg > 1) {
+    const StateView seg = seg_view(seg_f, f0, sp.nseg);
+    e = segment_states(f, WV_FWD_STATE_BF16, sp, S0, seg, (float*)(w + p.off_decf), BH, st);
+    if (e == hipSuccess) e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, seg, ffin, BH, st);
+  } else {
+    e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, f0, ffin, BH, st);
+  }
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq walk");
+
+  // 2. The state gradient, backwards in time: U_t = e^{g_{t+1}} U_{t+1} +
+  //    q_t^T dO_t from U = dS_T, i.e. the forward recurrence over the
+  //    reversed tokens with keys q, values a dv-half of dO and the log-decay
+  //    shifted by one token.
   WalkArgs r{};
-  r.X = q;
-  r.Y = dO;
-  r.g = g;
+  r.X = tok_view(q, 2, dims, DK, 0, true);
+  r.Y = tok_view(dO, 2, dims, DV, hw, true);
+  r.g = g + (dims->T - 1) * dims->H;
+  r.gsb = dims->T * dims->H;
+  r.gsh = 1;
+  r.gst = -(int64_t)dims->H;
+  r.gshift = 1;
   r.B = dims->B;
   r.T = dims->T;
   r.H = dims->H;
-  r.st_dc = w + p.off_dsdc;
-  r.st_cd = w + p.off_dscd;
-  e = run_walk(r, WV_REV_BF16, p.ns, p.nseg_r, p.cps_r, p.n_chunks, true, dS_T, dS0, seg_states, seg_decay, BH, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd state-gradient walk");
-  // 3. per-chunk gradients
-  BwdArgs b{};
-  b.q = q; b.k = k; b.v = v; b.dO = dO; b.g = g;
-  b.s_dc = w + p.off_s;
-  b.ds_dc = w + p.off_dsdc;
-  b.ds_cd = w + p.off_dscd;
-  b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg;
-  b.chunk_r = (float*)(w + p.off_r);
-  b.B = dims->B; b.T = dims->T; b.H = dims->H; b.n_chunks = p.n_chunks;
-  e = launch_bwd_chunks(b, dims->out_dtype == GLA_BF16, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd chunk kernel");
-  // 4. d-log-decay: add later chunks and <dS_T, S_T>
-  e = launch_dg_finish(dg, b.chunk_r, dS_T, S_T, dims->B, dims->T, dims->H, p.n_chunks, st);
+  const StateView r0 = state_plain(const_cast<float*>(dS_T), hw);
+  StateView rseg = r0;
+  if (sp.nseg > 1) {
+    rseg = seg_view(seg_r, r0, sp.nseg);
+    e = segment_states(r, WV_FWD_STATE_BF16, sp, dS_T, rseg, (float*)(w + p.off_decr), BH, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd state-gradient segments");
+  }
+  // 2a. dv: queries k, outputs dv (a dv-half per slice); the final state is
+  //     the gradient leaving the first token (dS0 after its decay, below).
+  WalkArgs rv = r;
+  rv.Q = tok_view(k, 2, dims, DK, 0, true);
+  rv.O = tok_view(dv, osz, dims, DV, hw, true);
+  e = walk_segments(rv, out_variant, sp, rseg, state_plain(dS0, hw), BH, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dv walk");
+  // 2b. dk: keys a dv-half of dO, values q (the state is the transpose),
+  //     queries the same half of v; partial sums of dk.
+  WalkArgs rk = r;
+  rk.X = tok_view(dO, 2, dims, DV, hw, true);
+  rk.Y = tok_view(q, 2, dims, DK, 0, true);
+  rk.Q = tok_view(v, 2, dims, DV, hw, true);
+  rk.O = part_view(dk_part, true);
+  StateView rkseg = rseg;
+  rkseg.sx = rseg.sy;
+  rkseg.sy = rseg.sx;
+  e = walk_segments(rk, WV_FWD_OUT_BF16_F32, sp, rkseg, StateView{}, BH, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dk walk");
+
+  // 3. dq, dk from the partial sums; q.dq - k.dk and its in-chunk suffix sums
+  BwdFinishArgs fa{};
+  fa.q = q;
+  fa.k = k;
+  fa.dq_part = dq_part;
+  fa.dk_part = dk_part;
+  fa.dq = dq;
+  fa.dk = dk;
+  fa.dg = dg;
+  fa.chunk_r = (float*)(w + p.off_r);
+  fa.B = dims->B;
+  fa.T = dims->T;
+  fa.H = dims->H;
+  fa.n_chunks = sp.n_chunks;
+  e = launch_bwd_finish(fa, dims->out_dtype == GLA_BF16, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd finish");
+  // 4. d-log-decay: add later chunks and <dS_T, S_T>; dS0 through the first decay
+  e = launch_dg_finish(dg, fa.chunk_r, dS_T, S_T, dS0, g, dims->B, dims->T, dims->H, sp.n_chunks, st);
   return device_err(e, "gla_chunk_bwd dg finish");
 }
 

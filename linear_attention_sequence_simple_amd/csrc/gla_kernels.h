@@ -9,7 +9,7 @@ constexpr int CH = 128;   // chunk length (tokens)
 constexpr int DK = 96;    // key/query width per head
 constexpr int DV = 192;   // value width per head
 
-enum WalkMode { WALK_FWD_OUT = 0, WALK_FWD_STATE = 1, WALK_REV = 2 };
+enum WalkMode { WALK_FWD_OUT = 0, WALK_FWD_STATE = 1 };
 
 enum WalkVariant {
   WV_FWD_OUT_BF16_BF16 = 0,
@@ -18,26 +18,41 @@ enum WalkVariant {
   WV_FWD_OUT_F32_BF16 = 3,
   WV_FWD_STATE_BF16 = 4,
   WV_FWD_STATE_F32 = 5,
-  WV_REV_BF16 = 6,
 };
 
-// Arguments of one walk launch.  Tensors are [B,T,H,D] row-major; states are
-// [DK][DV] float32 blocks addressed as base + bh*bh_stride + seg*seg_stride.
+// A token tensor as one walk sees it: column j of dv-slice s of token t (in
+// walk order), batch b, head h is at
+//     p + b*sb + h*sh + t*st + s*ss + j        (elements)
+// A negative st walks a [B,T,H,D] tensor backwards in time.
+struct TokView {
+  const void* p;
+  int64_t sb, sh, st, ss;
+};
+
+// A state block: element (x index i, y index j) of dv-slice s of (batch-head
+// bh, segment seg) is at p + bh*sbh + seg*sseg + s*ss + i*sx + j*sy, where x
+// indexes the key-side width and y the value-side width of the walk.
+struct StateView {
+  float* p;
+  int64_t sbh, sseg, ss, sx, sy;
+};
+
+// Arguments of one walk launch: the recurrence Z_t = e^{g_t} Z_{t-1} + x_t^T y_t
+// over the walk's tokens, optionally with the outputs
+// o_t = q_t Z_t (queries Q, written to O).
 struct WalkArgs {
-  const void* X;        // forward: keys; reverse: queries      [B,T,H,DK]
-  const void* Y;        // forward: values; reverse: dO         [B,T,H,DV]
-  const void* Q;        // forward with output: queries         [B,T,H,DK]
-  const float* g;       // log-decay                            [B,T,H]
-  const float* zinit;   // initial state or null (zero)
-  int64_t zinit_bh_stride, zinit_seg_stride;
-  float* zfin;          // final state or null
-  int64_t zfin_bh_stride, zfin_seg_stride;
+  TokView X;            // keys            (width 96)
+  TokView Y;            // values          (width 96 per slice; 64 for fp32 inputs)
+  TokView Q;            // queries         (width 96), with output only
+  TokView O;            // outputs         (width of Y), with output only
+  const float* g;       // log-decay of walk token t: g[b*gsb + h*gsh + (t - gshift)*gst],
+  int64_t gsb, gsh, gst;  // zero for t < gshift
+  int gshift;
+  StateView zinit;      // initial state (p null: zero)
+  StateView zfin;       // final state (p null: not written)
   int zfin_only_seg;    // -1: every segment writes; else only that segment
   float* seg_decay;     // per-segment total log2-decay or null
   int64_t seg_decay_bh_stride;
-  void* O;              // output [B,T,H,DV] (forward with output)
-  void* st_dc;          // per-chunk entering state, bf16 fragments (m=d, k=c), or null
-  void* st_cd;          // per-chunk entering state, bf16 fragments (m=c, k=d), or null
   int64_t B, T;
   int H, n_chunks, cps, ns, nseg_launch, seg_offset;
 };
@@ -55,18 +70,18 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, hipStream_t st);
 
-// Chunk-parallel backward and the d-log-decay finish: see gla_bwd.hip.
-struct BwdArgs {
-  const void* q; const void* k; const void* v; const void* dO; const float* g;
-  const void* s_dc;     // forward entering states, fragments (m=d, k=c)   [BH][N]
-  const void* ds_dc;    // state gradient leaving each chunk (m=d, k=c)    [BH][N]
-  const void* ds_cd;    // same, (m=c, k=d)                                 [BH][N]
-  void* dq; void* dk; void* dv; float* dg;
-  float* chunk_r;       // per-chunk sum of q.dq - k.dk                     [BH][N]
+// Backward finish: see gla_bwd.hip.
+struct BwdFinishArgs {
+  const void* q; const void* k;       // [B,T,H,DK] bf16
+  const float* dq_part;               // [2][B,T,H,DK] fp32 partial sums of dq
+  const float* dk_part;               // [2][B,T,H,DK] fp32 partial sums of dk
+  void* dq; void* dk;                 // [B,T,H,DK] results
+  float* dg;                          // [B,T,H] in-chunk suffix sums of q.dq - k.dk
+  float* chunk_r;                     // [BH][N] per-chunk totals
   int64_t B, T; int H, n_chunks;
 };
-hipError_t launch_bwd_chunks(const BwdArgs& a, int out_bf16, hipStream_t st);
-hipError_t launch_dg_finish(float* dg, const float* chunk_r, const float* dS_T, const float* S_T,
-                            int64_t B, int64_t T, int H, int n_chunks, hipStream_t st);
+hipError_t launch_bwd_finish(const BwdFinishArgs& a, int out_bf16, hipStream_t st);
+hipError_t launch_dg_finish(float* dg, const float* chunk_r, const float* dS_T, const float* S_T, float* dS0,
+                            const float* g, int64_t B, int64_t T, int H, int n_chunks, hipStream_t st);
 
 }  // namespace gla

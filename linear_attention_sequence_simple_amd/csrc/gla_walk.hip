@@ -9,9 +9,9 @@
 //     O   = (Q K^T (.) M) V + diag(Lambda) Q S_n
 //     S_n+1 = Gamma S_n + (diag(kappa) K)^T V
 // which follows from unrolling S_t = e^{g_t} S_{t-1} + k_t^T v_t over the
-// chunk.  The reverse walk of the backward carries the state gradient
-//     dS_n = Gamma dS_n+1 + (diag(Lambda) Q)^T dO
-// with the same code (X = Q, Y = dO, weights Lambda, chunks in reverse).
+// chunk.  The walks read their tensors through strided views (batch, head,
+// token and slice strides), so the backward runs the same kernels on other
+// operand roles and, with negative token strides, backwards in time.
 //
 // The state is held transposed, Z^T[c][d], as 32x32 tiles (c rows, d cols)
 // spread over the "state" waves.  The prefill with output runs 8 waves, two
@@ -98,8 +98,23 @@ struct WalkSmem {
 
 __device__ __forceinline__ int utab_off(int I) { return I == 1 ? 0 : I == 2 ? 32 : 96; }
 
-// Rows [t0, t0+128) of a [B,T,H,D] tensor, columns [col0, col0+W), as 16-byte
-// pieces held in registers; rows past T read as zero.
+// Rows [t0, t0+nrows) of a strided token view start, in memory order, at
+// tile_base = base + (t0 + rref) * stride with rref = nrows-1 for a negative
+// stride (time read backwards) and 0 otherwise; row r, column c then sits at
+// the non-negative byte offset row_offset from it.  The base is the same for
+// the whole workgroup and the offset fits 32 bits, which keeps the per-lane
+// address in one register.
+template <class T>
+__device__ __forceinline__ const char* tile_base(const T* base, int64_t stride, int64_t t0, int nrows) {
+  return (const char*)(base + (t0 + (stride < 0 ? nrows - 1 : 0)) * stride);
+}
+template <class T>
+__device__ __forceinline__ uint32_t row_offset(int r, int c, int64_t stride, int nrows) {
+  return (uint32_t)(((r - (stride < 0 ? nrows - 1 : 0)) * (int)stride + c) * (int)sizeof(T));
+}
+
+// Rows [t0, t0+128) of a token view, as 16-byte pieces held in registers;
+// rows past T read as zero.
 template <class T, int WCOLS, int NTHR>
 struct TileRegs {
   // loader threads are numbered 0..NTHR-1 (the state waves of the workgroup)
@@ -111,10 +126,8 @@ struct TileRegs {
   __device__ __forceinline__ void load_piece(int i, const T* base, int64_t row_stride, int t0, int64_t T_len) {
     const int p = (threadIdx.x & (NTHR - 1)) + NTHR * i;
     const int row = p / PPR, cp = p % PPR;
-    if (p < NP && t0 + row < T_len)
-      r[i] = *(const uint4*)(base + (int64_t)(t0 + row) * row_stride + cp * EPP);
-    else
-      r[i] = make_uint4(0, 0, 0, 0);
+    r[i] = (p < NP && t0 + row < T_len) ? *(const uint4*)(base + (int64_t)(t0 + row) * row_stride + cp * EPP)
+                                        : make_uint4(0, 0, 0, 0);
   }
   __device__ __forceinline__ void load(const T* base, int64_t row_stride, int t0, int64_t T_len) {
 #pragma unroll
@@ -165,7 +178,6 @@ template <class TIn, class TOut, int NC, int MODE, int W>
 __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm,
                                           int b, int h, int slice, int seg) {
   constexpr bool OUT = MODE == WALK_FWD_OUT;
-  constexpr bool REV = MODE == WALK_REV;
   using S = WalkSmem<TIn, NC, OUT>;
   using FT = typename Frag<TIn>::type;
   constexpr int SUB = Frag<TIn>::SUB;
@@ -180,13 +192,12 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 
   const int lane = lane_id();
   const int g2 = lane >> 5;
-  const int c0 = slice * DVS;
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t T = a.T;
-  const TIn* Xb = (const TIn*)a.X + (int64_t)b * T * a.H * DK + (int64_t)h * DK;
-  const TIn* Yb = (const TIn*)a.Y + (int64_t)b * T * a.H * DV + (int64_t)h * DV + c0;
-  const TIn* Qb = OUT ? (const TIn*)a.Q + (int64_t)b * T * a.H * DK + (int64_t)h * DK : nullptr;
-  const float* gb = a.g + (int64_t)b * T * a.H + h;
+  const TIn* Xb = (const TIn*)a.X.p + b * a.X.sb + h * a.X.sh + slice * a.X.ss;
+  const TIn* Yb = (const TIn*)a.Y.p + b * a.Y.sb + h * a.Y.sh + slice * a.Y.ss;
+  const TIn* Qb = OUT ? (const TIn*)a.Q.p + b * a.Q.sb + h * a.Q.sh + slice * a.Q.ss : nullptr;
+  const float* gb = a.g + b * a.gsb + h * a.gsh;
 
   const int gseg = seg + a.seg_offset;
   const int n_begin = gseg * a.cps;
@@ -196,17 +207,15 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   // ---- state tiles Z^T (c rows, d columns): initial state or zero
   f32x16 z[NT > 0 ? NT : 1];
   {
-    const float* zi = a.zinit ? a.zinit + bh * a.zinit_bh_stride + (int64_t)gseg * a.zinit_seg_stride : nullptr;
+    const StateView& zv = a.zinit;
+    const float* zi = zv.p ? zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss : nullptr;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        f32x4 v = zi ? load4f(zi + (int64_t)d * DV + c0 + 32 * cb + 8 * qq + 4 * g2) : f32x4{0, 0, 0, 0};
-        z[t][4 * qq + 0] = v[0]; z[t][4 * qq + 1] = v[1];
-        z[t][4 * qq + 2] = v[2]; z[t][4 * qq + 3] = v[3];
-      }
+      for (int r = 0; r < 16; ++r)
+        z[t][r] = zi ? zi[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] : 0.f;
     }
   }
 
@@ -226,16 +235,16 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     constexpr int B = decltype(bc)::value % DEPTH;
     const int t0 = n * CH;
     if constexpr (LOADER) {
-      px[B].load(Xb, (int64_t)a.H * DK, t0, T);
-      py[B].load(Yb, (int64_t)a.H * DV, t0, T);
-      if constexpr (OUT && !COMP) pq[B].load(Qb, (int64_t)a.H * DK, t0, T);
+      px[B].load(Xb, a.X.st, t0, T);
+      py[B].load(Yb, a.Y.st, t0, T);
+      if constexpr (OUT && !COMP) pq[B].load(Qb, a.Q.st, t0, T);
     }
   };
   auto prefetch_q = [&](int n) {
     const int t0 = n * CH;
     if constexpr (OUTW && COMP) {
       const int64_t t = t0 + 32 * W + (lane & 31);
-      const bf16* qr = (const bf16*)Qb + t * a.H * DK + 8 * g2;
+      const bf16* qr = (const bf16*)Qb + t * a.Q.st + 8 * g2;
 #pragma unroll
       for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
@@ -252,13 +261,14 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     if (W == 0) {
       const int64_t t0 = (int64_t)n * CH;
       const int64_t ta = t0 + 2 * lane, tb = ta + 1, tc = t0 + 127 - 2 * lane, td = tc - 1;
-      gx0 = ta < T ? gb[ta * a.H] : 0.f;
-      gx1 = tb < T ? gb[tb * a.H] : 0.f;
-      gm0 = tc < T ? gb[tc * a.H] : 0.f;
-      gm1 = td < T ? gb[td * a.H] : 0.f;
+      const int sh = a.gshift;
+      gx0 = (ta < T && ta >= sh) ? gb[(ta - sh) * a.gst] : 0.f;
+      gx1 = (tb < T && tb >= sh) ? gb[(tb - sh) * a.gst] : 0.f;
+      gm0 = (tc < T && tc >= sh) ? gb[(tc - sh) * a.gst] : 0.f;
+      gm1 = (td < T && td >= sh) ? gb[(td - sh) * a.gst] : 0.f;
     }
   };
-  auto step_of = [&](int i) { return REV ? n_end - 1 - i : n_begin + i; };
+  auto step_of = [&](int i) { return n_begin + i; };
   if (nloc > 0) {
     prefetch(I0, step_of(0));
     prefetch_q(step_of(0));
@@ -269,7 +279,6 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   }
 
   float decay_sum = 0.f;
-  const bool store_dc = a.st_dc != nullptr, store_cd = a.st_cd != nullptr;
 
   auto body = [&](auto bc, int it) {
     constexpr int B = decltype(bc)::value % DEPTH;    // register buffer of this chunk
@@ -282,7 +291,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       py[B].template store<S::PY>(sm.y);
       if constexpr (OUT && !COMP) pq[B].template store<S::PQ>(sm.q);
       if constexpr (COMP)
-        px[B].template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, REV ? dc.lam : dc.kap);
+        px[B].template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, dc.kap);
     }
     // chunk it+DEPTH goes into this buffer now that it is staged
     if (it + DEPTH < nloc) prefetch(bc, step_of(it + DEPTH));
@@ -291,7 +300,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       for (int kb = 0; kb < 3; ++kb) { qcur[kb][0] = qnxt[kb][0]; qcur[kb][1] = qnxt[kb][1]; }
     }
     if (it + 1 < nloc) prefetch_q(step_of(it + 1));
-    if (OUT || store_dc || store_cd) {
+    if (OUT) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
@@ -310,33 +319,6 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     }
     __syncthreads();                                   // tiles and state copy visible
     decay_sum += dc.blast;
-
-    if constexpr (COMP) {
-      // Per-chunk state export for the backward: [hi | lo] bf16 fragment blocks.
-      if (store_dc || store_cd) {
-        const int64_t base = (bh * a.n_chunks + n) * (int64_t)(2 * DK * DV);
-        if (store_dc) {  // fragments (db, kc): S[d = 32db + l%32][c = 16kc + 8g + e]
-          constexpr int NF = 3 * (DVS / 16);
-          for (int f = U; f < NF; f += 4) {
-            const int db = f / (DVS / 16), kcl = f % (DVS / 16);
-            const int kc = c0 / 16 + kcl;
-            bf16* dst = (bf16*)a.st_dc + base + ((int64_t)(db * (DV / 16) + kc) * 64 + lane) * 8;
-            *(bf16x8*)dst = sfrag_kcN_any((const bf16*)sm.z, 32 * db, 16 * kcl, 0);
-            *(bf16x8*)(dst + DK * DV) = sfrag_kcN_any((const bf16*)sm.zl, 32 * db, 16 * kcl, 0);
-          }
-        }
-        if (store_cd) {  // fragments (cb, kd): S[d = 16kd + 8g + e][c = 32cb + l%32]
-          constexpr int NF = NC * 6;
-          for (int f = U; f < NF; f += 4) {
-            const int cbl = f / 6, kd = f % 6;
-            const int cb = c0 / 32 + cbl;
-            bf16* dst = (bf16*)a.st_cd + base + ((int64_t)(cb * 6 + kd) * 64 + lane) * 8;
-            *(bf16x8*)dst = sfrag_krN_any((const bf16*)sm.z, 32 * (kd >> 1), 32 * cbl, kd & 1);
-            *(bf16x8*)(dst + DK * DV) = sfrag_krN_any((const bf16*)sm.zl, 32 * (kd >> 1), 32 * cbl, kd & 1);
-          }
-        }
-      }
-    }
 
 
     if constexpr (OUTW) {
@@ -478,7 +460,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       }
       const int64_t trow = (int64_t)n * CH + il;
       if (trow < T) {
-        TOut* op = (TOut*)a.O + (((int64_t)b * T + trow) * a.H + h) * DV + c0 + 4 * g2;
+        TOut* op = (TOut*)a.O.p + b * a.O.sb + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
@@ -491,7 +473,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     // State update: Z^T = Gamma Z^T + Y^T (w X), contraction over the chunk's tokens.
     if constexpr (NT > 0) {
       const float gam = dc.gam;
-      const float* wts = REV ? dc.lam : dc.kap;
+      const float* wts = dc.kap;
 #pragma unroll
       for (int t = 0; t < NT; ++t) z[t] *= gam;
       constexpr int DB_LO = (NT >= 3) ? 0 : (T0 % 3);
@@ -563,16 +545,15 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   }
 
   // ---- final state
-  if (a.zfin && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
-    float* zo = a.zfin + bh * a.zfin_bh_stride + (int64_t)gseg * a.zfin_seg_stride;
+  if (a.zfin.p && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
+    const StateView& zv = a.zfin;
+    float* zo = zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        store4(zo + (int64_t)d * DV + c0 + 32 * cb + 8 * qq + 4 * g2,
-               f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]});
+      for (int r = 0; r < 16; ++r) zo[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] = z[t][r];
     }
   }
   if (a.seg_decay && slice == 0 && threadIdx.x == 0)
@@ -611,13 +592,12 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
 
   const int lane = lane_id();
   const int g2 = lane >> 5;
-  const int c0 = slice * DVS;
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t T = a.T;
-  const bf16* Xb = (const bf16*)a.X + (int64_t)b * T * a.H * DK + (int64_t)h * DK;
-  const bf16* Yb = (const bf16*)a.Y + (int64_t)b * T * a.H * DV + (int64_t)h * DV + c0;
-  const bf16* Qb = (const bf16*)a.Q + (int64_t)b * T * a.H * DK + (int64_t)h * DK;
-  const float* gb = a.g + (int64_t)b * T * a.H + h;
+  const bf16* Xb = (const bf16*)a.X.p + b * a.X.sb + h * a.X.sh + slice * a.X.ss;
+  const bf16* Yb = (const bf16*)a.Y.p + b * a.Y.sb + h * a.Y.sh + slice * a.Y.ss;
+  const bf16* Qb = (const bf16*)a.Q.p + b * a.Q.sb + h * a.Q.sh + slice * a.Q.ss;
+  const float* gb = a.g + b * a.gsb + h * a.gsh;
   const int gseg = seg + a.seg_offset;
   const int n_begin = gseg * a.cps;
   const int n_end = min(a.n_chunks, n_begin + a.cps);
@@ -626,17 +606,15 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   // ---- state tiles Z^T (c rows, d columns): initial state or zero
   f32x16 z[NT > 0 ? NT : 1];
   {
-    const float* zi = a.zinit ? a.zinit + bh * a.zinit_bh_stride + (int64_t)gseg * a.zinit_seg_stride : nullptr;
+    const StateView& zv = a.zinit;
+    const float* zi = zv.p ? zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss : nullptr;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        f32x4 v = zi ? load4f(zi + (int64_t)d * DV + c0 + 32 * cb + 8 * qq + 4 * g2) : f32x4{0, 0, 0, 0};
-        z[t][4 * qq + 0] = v[0]; z[t][4 * qq + 1] = v[1];
-        z[t][4 * qq + 2] = v[2]; z[t][4 * qq + 3] = v[3];
-      }
+      for (int r = 0; r < 16; ++r)
+        z[t][r] = zi ? zi[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] : 0.f;
     }
   }
 
@@ -646,11 +624,12 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   uint4 qr[OUTW ? 6 : 1];
   auto load_q = [&](int n) {
     if constexpr (OUTW) {
+      const int64_t t0 = (int64_t)n * CH + 32 * W;
+      const char* tile = tile_base(Qb, a.Q.st, t0, 32);
 #pragma unroll
       for (int i = 0; i < 6; ++i) {
         const int p = lane + 64 * i, row = p / 12, cp = p % 12;
-        const int64_t t = (int64_t)n * CH + 32 * W + row;
-        qr[i] = t < T ? *(const uint4*)(Qb + t * a.H * DK + cp * 8) : make_uint4(0, 0, 0, 0);
+        qr[i] = t0 + row < T ? *(const uint4*)(tile + row_offset<bf16>(row, cp * 8, a.Q.st, 32)) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -684,17 +663,18 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
     if (W == 0) {
       const int64_t t0 = (int64_t)n * CH;
       const int64_t ta = t0 + 2 * lane, tb = ta + 1, tc = t0 + 127 - 2 * lane, td = tc - 1;
-      gx0 = ta < T ? gb[ta * a.H] : 0.f;
-      gx1 = tb < T ? gb[tb * a.H] : 0.f;
-      gm0 = tc < T ? gb[tc * a.H] : 0.f;
-      gm1 = td < T ? gb[td * a.H] : 0.f;
+      const int sh = a.gshift;
+      gx0 = (ta < T && ta >= sh) ? gb[(ta - sh) * a.gst] : 0.f;
+      gx1 = (tb < T && tb >= sh) ? gb[(tb - sh) * a.gst] : 0.f;
+      gm0 = (tc < T && tc >= sh) ? gb[(tc - sh) * a.gst] : 0.f;
+      gm1 = (td < T && td >= sh) ? gb[(td - sh) * a.gst] : 0.f;
     }
   };
 
   if (nloc > 0) {
     if constexpr (!OUTW) {
-      px.load(Xb, (int64_t)a.H * DK, n_begin * CH, T);
-      py.load(Yb, (int64_t)a.H * DV, n_begin * CH, T);
+      px.load(Xb, a.X.st, n_begin * CH, T);
+      py.load(Yb, a.Y.st, n_begin * CH, T);
     }
     load_q(n_begin);
     load_g(n_begin);
@@ -802,11 +782,11 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
     } else {
       gam = dc.gam;
       py.template store<S::PY>(sm.y);
-      if (it + 1 < nloc) py.load(Yb, (int64_t)a.H * DV, (n + 1) * CH, T);
+      if (it + 1 < nloc) py.load(Yb, a.Y.st, (n + 1) * CH, T);
 #pragma unroll
       for (int i = 0; i < decltype(px)::PER; ++i) {
         px.store_weighted_piece(i, (bf16*)sm.xh, (bf16*)sm.xl, dc.kap);
-        if (it + 1 < nloc) px.load_piece(i, Xb, (int64_t)a.H * DK, (n + 1) * CH, T);
+        if (it + 1 < nloc) px.load_piece(i, Xb, a.X.st, (n + 1) * CH, T);
       }
     }
     __syncthreads();                                   // weighted keys and values visible; queries, keys, state copy and tables read
@@ -837,6 +817,9 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
         // next phase 1): written in the accumulator layout, read back and
         // stored as row-contiguous 16-byte pieces.
         bf16* ot = sm.q + 32 * W * 96;
+        const bf16* ob = (const bf16*)a.O.p + b * a.O.sb + h * a.O.sh + slice * a.O.ss;
+        const int64_t t0 = (int64_t)n * CH + 32 * W;
+        char* tile = const_cast<char*>(tile_base(ob, a.O.st, t0, 32));
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
@@ -847,13 +830,12 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
         for (int i = 0; i < 6; ++i) {
           const int p = lane + 64 * i, row = p / 12, cp = p % 12;
           const uint4 v = *(const uint4*)(ot + swz96(row, cp * 8));
-          const int64_t t = (int64_t)n * CH + 32 * W + row;
-          if (t < T) *(uint4*)((bf16*)a.O + (((int64_t)b * T + t) * a.H + h) * DV + c0 + cp * 8) = v;
+          if (t0 + row < T) *(uint4*)(tile + row_offset<bf16>(row, cp * 8, a.O.st, 32)) = v;
         }
       } else {
         const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
         if (trow < T) {
-          TOut* op = (TOut*)a.O + (((int64_t)b * T + trow) * a.H + h) * DV + c0 + 4 * g2;
+          TOut* op = (TOut*)a.O.p + b * a.O.sb + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
 #pragma unroll
           for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
@@ -909,16 +891,15 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   }
 
   // ---- final state
-  if (a.zfin && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
-    float* zo = a.zfin + bh * a.zfin_bh_stride + (int64_t)gseg * a.zfin_seg_stride;
+  if (a.zfin.p && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
+    const StateView& zv = a.zfin;
+    float* zo = zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        store4(zo + (int64_t)d * DV + c0 + 32 * cb + 8 * qq + 4 * g2,
-               f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]});
+      for (int r = 0; r < 16; ++r) zo[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] = z[t][r];
     }
   }
   if (a.seg_decay && slice == 0 && threadIdx.x == 0)
@@ -1007,7 +988,6 @@ hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st) 
     case WV_FWD_OUT_F32_BF16: return launch_one<float, bf16, 2, WALK_FWD_OUT>(a, nwg, st);
     case WV_FWD_STATE_BF16: return launch_one<bf16, float, 3, WALK_FWD_STATE>(a, nwg, st);
     case WV_FWD_STATE_F32: return launch_one<float, float, 2, WALK_FWD_STATE>(a, nwg, st);
-    case WV_REV_BF16: return launch_one<bf16, float, 3, WALK_REV>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
