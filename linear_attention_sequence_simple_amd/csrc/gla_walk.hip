@@ -214,8 +214,17 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        z[t][r] = zi ? zi[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] : 0.f;
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c = 32 * cb + 8 * qq + 4 * g2;
+        if (!zi) {
+          for (int e = 0; e < 4; ++e) z[t][4 * qq + e] = 0.f;
+        } else if (zv.sy == 1) {              // 4 consecutive y: one 16-byte access
+          const f32x4 v = load4f(zi + d * zv.sx + c);
+          for (int e = 0; e < 4; ++e) z[t][4 * qq + e] = v[e];
+        } else {                              // consecutive lanes are consecutive in memory
+          for (int e = 0; e < 4; ++e) z[t][4 * qq + e] = zi[d * zv.sx + (c + e) * zv.sy];
+        }
+      }
     }
   }
 
@@ -553,7 +562,14 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) zo[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] = z[t][r];
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c = 32 * cb + 8 * qq + 4 * g2;
+        if (zv.sy == 1) {
+          store4(zo + d * zv.sx + c, f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]});
+        } else {
+          for (int e = 0; e < 4; ++e) zo[d * zv.sx + (c + e) * zv.sy] = z[t][4 * qq + e];
+        }
+      }
     }
   }
   if (a.seg_decay && slice == 0 && threadIdx.x == 0)
@@ -613,8 +629,17 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        z[t][r] = zi ? zi[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] : 0.f;
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c = 32 * cb + 8 * qq + 4 * g2;
+        if (!zi) {
+          for (int e = 0; e < 4; ++e) z[t][4 * qq + e] = 0.f;
+        } else if (zv.sy == 1) {              // 4 consecutive y: one 16-byte access
+          const f32x4 v = load4f(zi + d * zv.sx + c);
+          for (int e = 0; e < 4; ++e) z[t][4 * qq + e] = v[e];
+        } else {                              // consecutive lanes are consecutive in memory
+          for (int e = 0; e < 4; ++e) z[t][4 * qq + e] = zi[d * zv.sx + (c + e) * zv.sy];
+        }
+      }
     }
   }
 
@@ -899,7 +924,14 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
       const int d = 32 * db + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) zo[d * zv.sx + (32 * cb + 8 * (r >> 2) + 4 * g2 + (r & 3)) * zv.sy] = z[t][r];
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c = 32 * cb + 8 * qq + 4 * g2;
+        if (zv.sy == 1) {
+          store4(zo + d * zv.sx + c, f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]});
+        } else {
+          for (int e = 0; e < 4; ++e) zo[d * zv.sx + (c + e) * zv.sy] = z[t][4 * qq + e];
+        }
+      }
     }
   }
   if (a.seg_decay && slice == 0 && threadIdx.x == 0)
