@@ -162,11 +162,10 @@ void set_plan(WalkArgs& a, const SegPlan& sp) {
   a.cps = sp.cps;
 }
 
-// Segment pass 1 and scan: the state change of every segment but the last
-// from a zero state, then a scan over segments from z0, which leaves in
-// `seg` the state entering every segment.  z0 and seg share one layout.
-hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, const float* z0, StateView seg,
-                          float* seg_decay, int64_t BH, hipStream_t st) {
+// Segment pass 1: the walk of every segment but the last from a zero state,
+// writing each segment's state change into `seg` and its total decay into
+// seg_decay.
+WalkArgs pass1_args(WalkArgs a, const SegPlan& sp, StateView seg, float* seg_decay) {
   set_plan(a, sp);
   a.zinit = StateView{};
   a.zfin = seg;
@@ -175,7 +174,14 @@ hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, cons
   a.seg_decay_bh_stride = sp.nseg;
   a.nseg_launch = sp.nseg - 1;
   a.seg_offset = 0;
-  hipError_t e = launch_walk(a, state_variant, (int)(BH * sp.ns * (sp.nseg - 1)), st);
+  return a;
+}
+
+// Pass 1 and a scan over segments from z0, which leaves in `seg` the state
+// entering every segment.  z0 and seg share one layout.
+hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, const float* z0, StateView seg,
+                          float* seg_decay, int64_t BH, hipStream_t st) {
+  hipError_t e = launch_walk(pass1_args(a, sp, seg, seg_decay), state_variant, (int)(BH * sp.ns * (sp.nseg - 1)), st);
   if (e != hipSuccess) return e;
   return launch_seg_scan(seg.p, seg_decay, z0, BH, sp.nseg, 0, st);
 }
@@ -441,15 +447,6 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   f.H = dims->H;
   const StateView f0 = state_transposed(const_cast<float*>(S0), hw);
   const StateView ffin = state_transposed(dS_T ? S_T : nullptr, hw);
-  hipError_t e = hipSuccess;
-  if (sp.nseg > 1) {
-    const StateView seg = seg_view(seg_f, f0, sp.nseg);
-    e = segment_states(f, WV_FWD_STATE_BF16, sp, S0, seg, (float*)(w + p.off_decf), BH, st);
-    if (e == hipSuccess) e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, seg, ffin, BH, st);
-  } else {
-    e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, f0, ffin, BH, st);
-  }
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq walk");
 
   // 2. The state gradient, backwards in time: U_t = e^{g_{t+1}} U_{t+1} +
   //    q_t^T dO_t from U = dS_T, i.e. the forward recurrence over the
@@ -467,12 +464,23 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   r.T = dims->T;
   r.H = dims->H;
   const StateView r0 = state_plain(const_cast<float*>(dS_T), hw);
-  StateView rseg = r0;
+
+  // Segment states of both recurrences: their pass-1 walks share one launch.
+  hipError_t e = hipSuccess;
+  StateView fseg = f0, rseg = r0;
   if (sp.nseg > 1) {
+    fseg = seg_view(seg_f, f0, sp.nseg);
     rseg = seg_view(seg_r, r0, sp.nseg);
-    e = segment_states(r, WV_FWD_STATE_BF16, sp, dS_T, rseg, (float*)(w + p.off_decr), BH, st);
-    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd state-gradient segments");
+    float* dec_f = (float*)(w + p.off_decf);
+    float* dec_r = (float*)(w + p.off_decr);
+    const int n1 = (int)(BH * sp.ns * (sp.nseg - 1));
+    e = launch_state_walk_pair(pass1_args(f, sp, fseg, dec_f), n1, pass1_args(r, sp, rseg, dec_r), n1, st);
+    if (e == hipSuccess) e = launch_seg_scan(fseg.p, dec_f, S0, BH, sp.nseg, 0, st);
+    if (e == hipSuccess) e = launch_seg_scan(rseg.p, dec_r, dS_T, BH, sp.nseg, 0, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd segment states");
   }
+  e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, fseg, ffin, BH, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq walk");
   // 2a. dv: queries k, outputs dv (a dv-half per slice); the final state is
   //     the gradient leaving the first token (dS0 after its decay, below).
   WalkArgs rv = r;

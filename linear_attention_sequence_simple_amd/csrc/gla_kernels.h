@@ -58,6 +58,9 @@ struct WalkArgs {
 };
 
 hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st);
+// Two independent bf16 state-only walks in one launch (nwg0 + nwg1
+// workgroups).
+hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st);
 int walk_slices(int variant);
 hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, int64_t BH, int nseg, int rev,
                            hipStream_t st);

@@ -839,8 +839,9 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
       }
       if constexpr (std::is_same<TOut, bf16>::value) {
         // Through this wave's own rows of the query tile (free until the
-        // next phase 1): written in the accumulator layout, read back and
-        // stored as row-contiguous 16-byte pieces.
+        // next phase 1; the wave's LDS accesses execute in order): written
+        // in the accumulator layout, read back and stored as row-contiguous
+        // 16-byte pieces.
         bf16* ot = sm.q + 32 * W * 96;
         const bf16* ob = (const bf16*)a.O.p + b * a.O.sb + h * a.O.sh + slice * a.O.ss;
         const int64_t t0 = (int64_t)n * CH + 32 * W;
@@ -938,16 +939,16 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
     a.seg_decay[bh * a.seg_decay_bh_stride + gseg] = decay_sum;
 }
 
+// The walk of workgroup `local` of a launch of `nwg` workgroups.
 template <class TIn, class TOut, int NC, int MODE>
-__global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkArgs a) {
-  __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
+__device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm, int local,
+                                           int nwg) {
   // Work item order: slice fastest, then segment, head, batch.  Consecutive
   // items are placed on the same XCD (the dispatcher deals workgroups to the
   // 8 XCDs round-robin), so the dv-slices of one head and neighbouring heads
   // share that XCD's L2.
-  const int nwg = gridDim.x;
-  int wid = blockIdx.x;
-  if ((nwg & 7) == 0) wid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  int wid = local;
+  if ((nwg & 7) == 0) wid = (local & 7) * (nwg >> 3) + (local >> 3);
   const int slice = wid % a.ns;
   int rest = wid / a.ns;
   const int seg = rest % a.nseg_launch;
@@ -986,6 +987,26 @@ __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkA
   }
 }
 
+
+template <class TIn, class TOut, int NC, int MODE>
+__global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkArgs a) {
+  __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
+  walk_block<TIn, TOut, NC, MODE>(a, sm, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Two independent state walks of one kind side by side: workgroups [0, nwg0)
+// run a0, the rest a1.  Each walk orders its own workgroups; the XCD
+// placement matches the dispatcher's when nwg0 is a multiple of 8.
+template <class TIn, int NC>
+__global__ void __launch_bounds__(WalkShape<WALK_FWD_STATE>::THREADS, 1)
+    walk_pair_kernel(WalkArgs a0, WalkArgs a1, int nwg0) {
+  __shared__ WalkSmem<TIn, NC, false> sm;
+  if ((int)blockIdx.x < nwg0)
+    walk_block<TIn, float, NC, WALK_FWD_STATE>(a0, sm, (int)blockIdx.x, nwg0);
+  else
+    walk_block<TIn, float, NC, WALK_FWD_STATE>(a1, sm, (int)blockIdx.x - nwg0, (int)gridDim.x - nwg0);
+}
+
 // Segment scan: buf[bh][s] holds the state change of segment s from a zero
 // state (pass 1); replace it by the state entering segment s.  decay[bh][s] is
 // the segment's total log2-decay.  Forward order starts from Z0, reverse order
@@ -1022,6 +1043,12 @@ hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st) 
     case WV_FWD_STATE_F32: return launch_one<float, float, 2, WALK_FWD_STATE>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st) {
+  hipLaunchKernelGGL((walk_pair_kernel<bf16, 3>), dim3(nwg0 + nwg1), dim3(WalkShape<WALK_FWD_STATE>::THREADS), 0,
+                     st, a0, a1, nwg0);
+  return hipGetLastError();
 }
 
 int walk_slices(int variant) {
