@@ -137,26 +137,26 @@ def _dev_inputs(torch, d, in_dtype):
 
 
 def _time_calls(torch, fn, steps, warmup):
-    """Per-call device time of fn() with HIP events on the current stream.
+    """Mean device time per call of fn(): HIP events on the current stream
+    bracket the `steps` timed calls, which run back to back.
 
-    A spin of the device is queued ahead of the timed calls, so the host-side
+    A spin of the device is queued ahead of the timed region, so the host-side
     argument marshalling of the binding never leaves the device idle between
-    an event and the launch it brackets: each event pair then times the
-    kernels of one call back to back, as the kernel trace does."""
+    calls; the events themselves sit outside the calls, so nothing is inserted
+    between the kernels being timed.  Returns (ms per call, wall seconds)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(steps * 5e5))             # ~0.2 ms of queue per call at 2.4 GHz
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
+    e0.record()
+    for _ in range(steps):
         fn()
-        b.record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]
-    return per, wall
+    return e0.elapsed_time(e1) / steps, wall
 
 
 def _rel_err(got, ref):
@@ -175,12 +175,11 @@ def bench_prefill(torch, gla, steps, warmup, parity=True):
     ws_bytes = gla.gla_workspace_size(gla.GLA_OP_FWD, dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     fn = lambda: gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T, workspace=ws)
-    per, wall = _time_calls(torch, fn, steps, warmup)
-    ms = float(np.mean(per))
+    ms, wall = _time_calls(torch, fn, steps, warmup)
     tokens = B * T
     nbytes = fwd_bytes(B, T, 2, 2)
     flops = FWD_FLOP_PER_TH * B * T * H
-    res = {"ms": ms, "ms_min": float(np.min(per)), "tokens_per_s": tokens / (ms * 1e-3), "bytes": nbytes,
+    res = {"ms": ms, "tokens_per_s": tokens / (ms * 1e-3), "bytes": nbytes,
            "flops": flops, "GBps": nbytes / (ms * 1e-3) / 1e9,
            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "launches": 1 if ws_bytes == 0 else 3,
            "wall_s": wall}
@@ -206,8 +205,7 @@ def bench_prefill_other(torch, gla, name, in_dtype, out_dtype, steps, warmup):
     o = torch.empty((B, T, H, DV), dtype=out_dtype, device=q.device)
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=q.device)
     fn = lambda: gla.gla_chunk_fwd(q, k, v, g, S0, out_dtype=out_dtype, o=o, S_T=S_T, workspace=ws)
-    per, _ = _time_calls(torch, fn, steps, warmup)
-    ms = float(np.mean(per))
+    ms, _ = _time_calls(torch, fn, steps, warmup)
     ib = 2 if in_dtype == torch.bfloat16 else 4
     ob = 2 if out_dtype == torch.bfloat16 else 4
     nbytes = fwd_bytes(B, T, ib, ob, s0=S0 is not None)
@@ -241,27 +239,26 @@ def bench_decode(torch, gla, layers=24, steps=64, warmup=1, parity=True):
     for _ in range(warmup):
         gla.gla_recurrent_step(scratch, *xs[0], out_dtype=torch.float32, o=outs[0])
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps * layers)]
+    # events bracket all launches (one step of every layer, steps times); a
+    # device spin queued ahead keeps host marshalling out of the timed region
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e6))
     t0 = time.perf_counter()
-    i = 0
+    e0.record()
     for s in range(steps):
         for l in range(layers):
-            a, b = ev[i]
-            a.record()
             gla.gla_recurrent_step(pools[l], *xs[s], out_dtype=torch.float32, o=outs[l])
-            b.record()
-            i += 1
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([a.elapsed_time(b) for a, b in ev])
-    ms_launch = float(per.mean())
+    ms_total = e0.elapsed_time(e1)
+    ms_launch = ms_total / (steps * layers)
     nbytes = decode_bytes(n)
     res = {"workload": f"decode step, {n} sequences x {layers} layers x {steps} steps, H=16, "
                        f"fp32 state [{n},16,96,192] per layer, bf16 q/k/v, fp32 o",
            "us_per_layer_step": ms_launch * 1e3, "GBps": nbytes / (ms_launch * 1e-3) / 1e9,
            "hbm_frac": nbytes / (ms_launch * 1e-3) / 1e9 / HBM_PEAK_GBS,
-           "tokens_per_s": n * steps / (per.sum() * 1e-3), "bytes_per_launch": nbytes,
+           "tokens_per_s": n * steps / (ms_total * 1e-3), "bytes_per_launch": nbytes,
            "launches": int(steps * layers), "wall_s": wall}
     if parity:
         import oracle
@@ -288,14 +285,15 @@ def bench_backward(torch, gla, steps, warmup):
     dims = gla.GlaDims(B, T, H, DK, DV, CH, gla.GLA_BF16, gla.GLA_BF16)
     ws = torch.empty(gla.gla_workspace_size(gla.GLA_OP_BWD, dims), dtype=torch.uint8, device=q.device)
     fn = lambda: gla.gla_chunk_bwd(q, k, v, g, dO, out_dtype=torch.bfloat16, workspace=ws)
-    per, _ = _time_calls(torch, fn, steps, warmup)
-    ms = float(np.mean(per))
+    ms, _ = _time_calls(torch, fn, steps, warmup)
     nbytes = bwd_bytes(B, T, 2, 2)
     flops = BWD_FLOP_PER_TH * B * T * H
     return {"workload": f"backward B={B} T={T} H=16 bf16 in/out, fp32 dg, S0 = dS_T = 0",
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "GBps_algorithmic": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "launches": 4 + 0}
+            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+            "kernels_per_call": "8: paired pass-1 state walks, 2 segment scans, dq/dv/dk walks, "
+                                "partial-sum finish, d-log-decay finish"}
 
 
 def src_digest():
