@@ -319,10 +319,9 @@ __device__ __forceinline__ float wave_shr1(float x) { return dpp_mov<0x138, 0xf>
 
 // Chunk decay tables in LDS, from the chunk's log-decay.  With b_i the
 // inclusive running sum of the clamped log-decay (in log2 units):
-//   b2[i]  = b_i,  lam[i] = 2^{b_i},  kap[i] = 2^{b_last - b_i},  gam = 2^{b_last}
+//   b2[i]  = b_i (so Lambda_i = 2^{b_i}),  kap[i] = 2^{b_last - b_i},  gam = 2^{b_last}
 struct DecayLds {
   float b2[CH];
-  float lam[CH];
   float kap[CH];
   float gam;
   float blast;
@@ -349,8 +348,6 @@ __device__ __forceinline__ void build_decay(DecayLds* d, float x0, float x1, flo
   const float blast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), 63));
   d->b2[2 * l] = b0;
   d->b2[2 * l + 1] = b1;
-  d->lam[2 * l] = exp2f(b0);
-  d->lam[2 * l + 1] = exp2f(b1);
   d->kap[127 - 2 * l] = exp2f(sr_ex);
   d->kap[126 - 2 * l] = exp2f(sr_ex + m0);
   if (l == 0) { d->gam = exp2f(blast); d->blast = blast; }

@@ -88,10 +88,9 @@ struct WalkSmem {
   TIn q[OUT ? CH * PQ : 8];               // queries
   TIn z[DK * PZ];                         // state entering the chunk, [d][c]
   TIn zl[COMP ? DK * PZ : 8];             // residual of its bf16 copy
-  // Decay tables: the other walks keep the current chunk's and the next
-  // one's (built a chunk ahead); the bf16 prefill rebuilds one set in the
-  // phase where nobody reads it.
-  static constexpr int NDEC = (OUT && COMP) ? 1 : 2;
+  // Decay tables of the current chunk and of the next one (built a chunk
+  // ahead).
+  static constexpr int NDEC = 2;
   DecayLds dec[NDEC];
   // utab[U(I) + j] = 2^{b_{32I} - b_j} for j < 32I (I = 1, 2, 3; U = 0, 32, 96):
   // the key-side factor of the decay between token blocks.
@@ -438,7 +437,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
             for (int cb = 0; cb < NC; ++cb)
               o[cb] = mfma(frag_kr(sm.z, S::PZ, 32 * kb, 32 * cb, s), qn[kb][s], o[cb]);
       }
-      const float lam = dc.lam[il];
+      const float lam = exp2f(dc.b2[il]);
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) o[cb] *= lam;
       if constexpr (COMP) {
@@ -582,17 +581,19 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 //   phase 1  output waves: stage their own 32 query rows, decay-masked scores
 //                          P from the queries and keys, and
 //                          O = diag(Lambda) (Q S_n) from the published bf16
-//                          value/residual copy of S_n
+//                          value/residual copy of S_n; wave 0 then builds
+//                          the decay tables of chunk n+1 in the other buffer
 //            state waves:  stage the values and the decay-weighted keys of
 //                          chunk n and request chunk n+1's values and keys
 //   barrier
 //   phase 2  output waves: O += P V, request their queries of chunk n+1,
-//                          store O; wave 0 builds the decay tables of n+1
+//                          store O
 //            state waves:  S_n+1 = Gamma S_n + (diag(kappa) K)^T V, publish
 //                          S_n+1, stage the keys of chunk n+1
 //   barrier
-// Every LDS tile (and the decay tables) is read in one phase only and
-// rewritten in the other, so one buffer of each suffices and the staging
+// Every LDS tile is read in one phase only and rewritten in the other, so
+// one buffer of each suffices (the decay tables, read in phase 1 and built
+// there for the next chunk, have two) and the staging
 // overlaps the products.  All tiles are read from memory with row-contiguous
 // 16-byte accesses, spread over both phases so that the workgroups on the
 // chip keep the memory busy instead of all loading at the same moment.
@@ -715,7 +716,8 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   float decay_sum = 0.f;
   for (int it = 0; it < nloc; ++it) {
     const int n = n_begin + it;
-    const DecayLds& dc = sm.dec[0];
+    const int cur = it & 1;
+    const DecayLds& dc = sm.dec[cur];
     decay_sum += dc.blast;
 
     // ================= phase 1
@@ -760,9 +762,15 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
         }
         __builtin_amdgcn_sched_barrier(0);   // one step of operands in flight
       }
-      const float lam = dc.lam[il];
+      const float lam = exp2f(dc.b2[il]);
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) o[cb] *= lam;
+      // wave 0 has the least product work: it builds the next chunk's decay
+      // tables here (that buffer's readers finished in the previous chunk)
+      if (W == 0 && it + 1 < nloc) {
+        build_decay(&sm.dec[cur ^ 1], gx0, gx1, gm0, gm1, sm.utab[cur ^ 1]);
+        if (it + 2 < nloc) load_g(n + 2);
+      }
       // Decay-masked scores P^T (keys j in rows, queries i in columns).  Off
       // the diagonal 2^{b_i - b_j} = 2^{b_i - b_{32W}} 2^{b_{32W} - b_j}.
       f32x16 acc[W + 1];
@@ -788,7 +796,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
 #pragma unroll
       for (int J = 0; J <= W; ++J) {
         if (J < W) {
-          const float* u = sm.utab[0] + utab_off(W) + 32 * J + 4 * g2;
+          const float* u = sm.utab[cur] + utab_off(W) + 32 * J + 4 * g2;
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             const f32x4 uu = *(const f32x4*)(u + 8 * qq);
@@ -874,10 +882,6 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
       // the next chunk's query loads (24 registers) after the products and stores
       __builtin_amdgcn_sched_barrier(0);
       if (it + 1 < nloc) load_q(n + 1);
-      if (W == 0 && it + 1 < nloc) {
-        build_decay(&sm.dec[0], gx0, gx1, gm0, gm1, sm.utab[0]);
-        if (it + 2 < nloc) load_g(n + 2);
-      }
     } else {
       // Z^T = Gamma Z^T + V^T (kappa K), over the 8 (token block, half) steps
 #pragma unroll
