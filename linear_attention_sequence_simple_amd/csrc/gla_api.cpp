@@ -102,9 +102,23 @@ int plan_segments(int64_t walkers, int n_chunks, const char* env) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct FwdPlan {
-  int variant, ns, nseg, cps, n_chunks;
+  int variant, ns, nseg, cps, n_chunks, fine;
   size_t ws_seg_states, ws_seg_decay, ws_total;
 };
+
+// Pass 1 may split each segment into `fine` parts: more, shorter state walks.
+// The bf16 state walk fits two workgroups per compute unit, so it splits
+// while that keeps at most two per unit and the parts stay whole chunks.
+int fine_factor(int64_t pass1_workgroups, int cps, bool bf16) {
+  int f = 1;
+  if (!bf16) return f;
+  while (f < 4 && cps % (2 * f) == 0 && pass1_workgroups * 2 * f <= 2 * kTargetWorkgroups) f *= 2;
+  return f;
+}
+
+// Segment-state entries: the states entering every fine part of every
+// segment but the last, and the state entering the last segment.
+int seg_entries(int nseg, int fine) { return (nseg - 1) * fine + 1; }
 
 FwdPlan plan_fwd(const gla_dims* d) {
   FwdPlan p{};
@@ -117,9 +131,11 @@ FwdPlan plan_fwd(const gla_dims* d) {
   p.cps = (p.n_chunks + p.nseg - 1) / p.nseg;
   p.nseg = (p.n_chunks + p.cps - 1) / p.cps;
   const int64_t BH = d->B * d->H;
+  p.fine = fine_factor(BH * p.ns * (p.nseg - 1), p.cps, in_bf16);
   if (p.nseg > 1) {
-    p.ws_seg_states = align256((size_t)BH * p.nseg * kStateElems * sizeof(float));
-    p.ws_seg_decay = align256((size_t)BH * p.nseg * sizeof(float));
+    const int ne = seg_entries(p.nseg, p.fine);
+    p.ws_seg_states = align256((size_t)BH * ne * kStateElems * sizeof(float));
+    p.ws_seg_decay = align256((size_t)BH * ne * sizeof(float));
   }
   p.ws_total = p.ws_seg_states + p.ws_seg_decay;
   return p;
@@ -144,17 +160,24 @@ TokView tok_view(const void* p, size_t esize, const gla_dims* d, int cols, int s
 StateView state_plain(float* p, int w) { return StateView{p, kStateElems, 0, w, DV, 1}; }
 StateView state_transposed(float* p, int w) { return StateView{p, kStateElems, 0, w, 1, DV}; }
 
-// The same layout for the per-segment states [BH][nseg][DK][DV].
-StateView seg_view(float* p, StateView lay, int nseg) {
+// The same layout for the per-segment states [BH][entries][DK][DV].
+StateView seg_view(float* p, StateView lay, int entries) {
   lay.p = p;
-  lay.sbh = (int64_t)nseg * kStateElems;
+  lay.sbh = (int64_t)entries * kStateElems;
   lay.sseg = kStateElems;
   return lay;
 }
 
 struct SegPlan {
-  int ns, nseg, cps, n_chunks;
+  int ns, nseg, cps, n_chunks, fine;
+  int entries() const { return seg_entries(nseg, fine); }
 };
+
+// The states entering the (coarse) segments inside the fine-part entries.
+StateView coarse(StateView seg, const SegPlan& sp) {
+  seg.sseg *= sp.fine;
+  return seg;
+}
 
 void set_plan(WalkArgs& a, const SegPlan& sp) {
   a.ns = sp.ns;
@@ -162,28 +185,31 @@ void set_plan(WalkArgs& a, const SegPlan& sp) {
   a.cps = sp.cps;
 }
 
-// Segment pass 1: the walk of every segment but the last from a zero state,
-// writing each segment's state change into `seg` and its total decay into
-// seg_decay.
+// Segment pass 1: the walk of every fine part of every segment but the last
+// from a zero state, writing each part's state change into `seg` and its
+// total decay into seg_decay.
+int pass1_workgroups(const SegPlan& sp, int64_t BH) { return (int)(BH * sp.ns * (sp.nseg - 1) * sp.fine); }
+
 WalkArgs pass1_args(WalkArgs a, const SegPlan& sp, StateView seg, float* seg_decay) {
   set_plan(a, sp);
+  a.cps = sp.cps / sp.fine;
   a.zinit = StateView{};
   a.zfin = seg;
   a.zfin_only_seg = -1;
   a.seg_decay = seg_decay;
-  a.seg_decay_bh_stride = sp.nseg;
-  a.nseg_launch = sp.nseg - 1;
+  a.seg_decay_bh_stride = sp.entries();
+  a.nseg_launch = (sp.nseg - 1) * sp.fine;
   a.seg_offset = 0;
   return a;
 }
 
-// Pass 1 and a scan over segments from z0, which leaves in `seg` the state
-// entering every segment.  z0 and seg share one layout.
+// Pass 1 and a scan over the parts from z0, which leaves in `seg` the state
+// entering every part.  z0 and seg share one layout.
 hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, const float* z0, StateView seg,
                           float* seg_decay, int64_t BH, hipStream_t st) {
-  hipError_t e = launch_walk(pass1_args(a, sp, seg, seg_decay), state_variant, (int)(BH * sp.ns * (sp.nseg - 1)), st);
+  hipError_t e = launch_walk(pass1_args(a, sp, seg, seg_decay), state_variant, pass1_workgroups(sp, BH), st);
   if (e != hipSuccess) return e;
-  return launch_seg_scan(seg.p, seg_decay, z0, BH, sp.nseg, 0, st);
+  return launch_seg_scan(seg.p, seg_decay, z0, BH, sp.entries(), 0, st);
 }
 
 // The walk of every segment from its entering state (zinit: the segment
@@ -219,14 +245,15 @@ BwdPlan plan_bwd(const gla_dims* d) {
   p.sp.nseg = plan_segments(BH * p.sp.ns, p.sp.n_chunks, "GLA_BWD_SEGMENTS");
   p.sp.cps = (p.sp.n_chunks + p.sp.nseg - 1) / p.sp.nseg;
   p.sp.nseg = (p.sp.n_chunks + p.sp.cps - 1) / p.sp.cps;
+  p.sp.fine = fine_factor(2 * BH * p.sp.ns * (p.sp.nseg - 1), p.sp.cps, true);   // two recurrences
   const size_t part = align256((size_t)2 * d->B * d->T * d->H * DK * sizeof(float));
   size_t off = 0;
   p.off_dq = off; off += part;
   p.off_dk = off; off += part;
   p.off_st = off; off += align256((size_t)BH * kStateElems * sizeof(float));
   p.off_r = off; off += align256((size_t)BH * p.sp.n_chunks * sizeof(float));
-  const size_t seg = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.nseg * kStateElems * sizeof(float)) : 0;
-  const size_t dec = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.nseg * sizeof(float)) : 0;
+  const size_t seg = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * kStateElems * sizeof(float)) : 0;
+  const size_t dec = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * sizeof(float)) : 0;
   p.off_segf = off; off += seg;
   p.off_segr = off; off += seg;
   p.off_decf = off; off += dec;
@@ -347,16 +374,16 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, con
   a.T = dims->T;
   a.H = dims->H;
   const int64_t BH = dims->B * dims->H;
-  const SegPlan sp{p.ns, p.nseg, p.cps, p.n_chunks};
+  const SegPlan sp{p.ns, p.nseg, p.cps, p.n_chunks, p.fine};
   const StateView z0 = state_plain(const_cast<float*>(S0), w), zfin = state_plain(S_T, w);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (p.nseg > 1) {
     char* wsb = (char*)ws;
-    const StateView seg = seg_view((float*)wsb, z0, p.nseg);
+    const StateView seg = seg_view((float*)wsb, z0, sp.entries());
     const int state_variant = dims->in_dtype == GLA_BF16 ? WV_FWD_STATE_BF16 : WV_FWD_STATE_F32;
     e = segment_states(a, state_variant, sp, S0, seg, (float*)(wsb + p.ws_seg_states), BH, st);
-    if (e == hipSuccess) e = walk_segments(a, p.variant, sp, seg, zfin, BH, st);
+    if (e == hipSuccess) e = walk_segments(a, p.variant, sp, coarse(seg, sp), zfin, BH, st);
   } else {
     e = walk_segments(a, p.variant, sp, z0, zfin, BH, st);
   }
@@ -469,15 +496,17 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   hipError_t e = hipSuccess;
   StateView fseg = f0, rseg = r0;
   if (sp.nseg > 1) {
-    fseg = seg_view(seg_f, f0, sp.nseg);
-    rseg = seg_view(seg_r, r0, sp.nseg);
+    fseg = seg_view(seg_f, f0, sp.entries());
+    rseg = seg_view(seg_r, r0, sp.entries());
     float* dec_f = (float*)(w + p.off_decf);
     float* dec_r = (float*)(w + p.off_decr);
-    const int n1 = (int)(BH * sp.ns * (sp.nseg - 1));
+    const int n1 = pass1_workgroups(sp, BH);
     e = launch_state_walk_pair(pass1_args(f, sp, fseg, dec_f), n1, pass1_args(r, sp, rseg, dec_r), n1, st);
-    if (e == hipSuccess) e = launch_seg_scan(fseg.p, dec_f, S0, BH, sp.nseg, 0, st);
-    if (e == hipSuccess) e = launch_seg_scan(rseg.p, dec_r, dS_T, BH, sp.nseg, 0, st);
+    if (e == hipSuccess) e = launch_seg_scan(fseg.p, dec_f, S0, BH, sp.entries(), 0, st);
+    if (e == hipSuccess) e = launch_seg_scan(rseg.p, dec_r, dS_T, BH, sp.entries(), 0, st);
     if (e != hipSuccess) return device_err(e, "gla_chunk_bwd segment states");
+    fseg = coarse(fseg, sp);
+    rseg = coarse(rseg, sp);
   }
   e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, fseg, ffin, BH, st);
   if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq walk");

@@ -81,13 +81,17 @@ struct WalkSmem {
   static constexpr int PY = DVS;
   static constexpr int PZ = DVS;
   static constexpr int PQ = DK;                    // fp32 queries: unpadded (LDS budget)
-  TIn x[CH * PX];                         // keys (reverse walk: queries), as loaded
+  // The bf16 state-only walks read only the weighted keys and the values, so
+  // they keep no raw keys and no state copy: about 76 KB, two workgroups per
+  // compute unit.
+  static constexpr bool RAWX = OUT || !COMP;
+  TIn x[RAWX ? CH * PX : 8];              // keys, as loaded
   TIn xh[COMP ? CH * PX : 8];             // decay-weighted keys: bf16 value ...
   TIn xl[COMP ? CH * PX : 8];             // ... and bf16 residual
   TIn y[CH * PY];                         // values (reverse walk: dO), this dv-slice
   TIn q[OUT ? CH * PQ : 8];               // queries
-  TIn z[DK * PZ];                         // state entering the chunk, [d][c]
-  TIn zl[COMP ? DK * PZ : 8];             // residual of its bf16 copy
+  TIn z[OUT ? DK * PZ : 8];               // state entering the chunk, [d][c]
+  TIn zl[(OUT && COMP) ? DK * PZ : 8];    // residual of its bf16 copy
   // Decay tables of the current chunk and of the next one (built a chunk
   // ahead).
   static constexpr int NDEC = 2;
@@ -297,7 +301,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     DecayLds& dc = sm.dec[cur];
     __syncthreads();            // previous chunk's LDS reads done; this chunk's decay tables visible
     if constexpr (LOADER) {
-      px[B].template store<S::PX>(sm.x);
+      if constexpr (S::RAWX) px[B].template store<S::PX>(sm.x);
       py[B].template store<S::PY>(sm.y);
       if constexpr (OUT && !COMP) pq[B].template store<S::PQ>(sm.q);
       if constexpr (COMP)
@@ -310,7 +314,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       for (int kb = 0; kb < 3; ++kb) { qcur[kb][0] = qnxt[kb][0]; qcur[kb][1] = qnxt[kb][1]; }
     }
     if (it + 1 < nloc) prefetch_q(step_of(it + 1));
-    if (OUT) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
@@ -993,8 +997,13 @@ __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, 
 }
 
 
+// The bf16 state-only walks fit two workgroups per compute unit (LDS), so
+// they are built for two waves per SIMD (256 registers each).
+template <class TIn, int MODE>
+constexpr int walk_waves_per_eu() { return (MODE == WALK_FWD_STATE && sizeof(TIn) == 2) ? 2 : 1; }
+
 template <class TIn, class TOut, int NC, int MODE>
-__global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkArgs a) {
+__global__ void __launch_bounds__(WalkShape<MODE>::THREADS, (walk_waves_per_eu<TIn, MODE>())) walk_kernel(WalkArgs a) {
   __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
   walk_block<TIn, TOut, NC, MODE>(a, sm, (int)blockIdx.x, (int)gridDim.x);
 }
@@ -1003,7 +1012,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, 1) walk_kernel(WalkA
 // run a0, the rest a1.  Each walk orders its own workgroups; the XCD
 // placement matches the dispatcher's when nwg0 is a multiple of 8.
 template <class TIn, int NC>
-__global__ void __launch_bounds__(WalkShape<WALK_FWD_STATE>::THREADS, 1)
+__global__ void __launch_bounds__(WalkShape<WALK_FWD_STATE>::THREADS, (walk_waves_per_eu<TIn, WALK_FWD_STATE>()))
     walk_pair_kernel(WalkArgs a0, WalkArgs a1, int nwg0) {
   __shared__ WalkSmem<TIn, NC, false> sm;
   if ((int)blockIdx.x < nwg0)
