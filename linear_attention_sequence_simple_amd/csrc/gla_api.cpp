@@ -215,8 +215,7 @@ hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, cons
 // The walk of every segment from its entering state (zinit: the segment
 // states, or the initial state when there is one segment); the final state
 // comes from the last segment.
-hipError_t walk_segments(WalkArgs a, int variant, const SegPlan& sp, StateView zinit, StateView zfin, int64_t BH,
-                         hipStream_t st) {
+WalkArgs segments_args(WalkArgs a, const SegPlan& sp, StateView zinit, StateView zfin) {
   set_plan(a, sp);
   a.zinit = zinit;
   a.zfin = zfin;
@@ -225,16 +224,36 @@ hipError_t walk_segments(WalkArgs a, int variant, const SegPlan& sp, StateView z
   a.seg_decay = nullptr;
   a.nseg_launch = sp.nseg;
   a.seg_offset = 0;
-  return launch_walk(a, variant, (int)(BH * sp.ns * sp.nseg), st);
+  return a;
 }
 
-// Backward workspace: fp32 partial sums of dq and dk over the two dv-halves
-// ([2][B,T,H,DK] each), the final forward state, per-chunk sums of the
-// log-decay gradient, and the segment states and decays of the forward and
-// the backward-in-time recurrences.
+hipError_t walk_segments(WalkArgs a, int variant, const SegPlan& sp, StateView zinit, StateView zfin, int64_t BH,
+                         hipStream_t st) {
+  return launch_walk(segments_args(a, sp, zinit, zfin), variant, (int)(BH * sp.ns * sp.nseg), st);
+}
+
+// A view moved by `elems` elements of `esize` bytes (a dv-half of a tensor).
+TokView shifted(TokView v, int64_t elems, size_t esize) {
+  if (v.p) v.p = (const char*)v.p + elems * (int64_t)esize;
+  return v;
+}
+StateView shifted(StateView v, int64_t elems) {
+  if (v.p) v.p += elems;
+  return v;
+}
+// One [B,T,H] float per token, read forwards or backwards in time.
+TokView token_floats(float* p, const gla_dims* d, bool backwards) {
+  TokView v = tok_view(p, 4, d, 1, 0, backwards);
+  return v;
+}
+
+// Backward workspace: fp32 sums of dq and dk over the first dv-half
+// ([B,T,H,DK] each), the dot products q.dq and k.dk ([B,T,H] each), the final
+// forward state, per-chunk sums of the log-decay gradient, and the segment
+// states and decays of the forward and the backward-in-time recurrences.
 struct BwdPlan {
   SegPlan sp;
-  size_t off_dq, off_dk, off_st, off_r, off_segf, off_segr, off_decf, off_decr, ws_total;
+  size_t off_dq, off_dk, off_rq, off_rk, off_st, off_r, off_segf, off_segr, off_decf, off_decr, ws_total;
 };
 
 BwdPlan plan_bwd(const gla_dims* d) {
@@ -246,10 +265,13 @@ BwdPlan plan_bwd(const gla_dims* d) {
   p.sp.cps = (p.sp.n_chunks + p.sp.nseg - 1) / p.sp.nseg;
   p.sp.nseg = (p.sp.n_chunks + p.sp.cps - 1) / p.sp.cps;
   p.sp.fine = fine_factor(2 * BH * p.sp.ns * (p.sp.nseg - 1), p.sp.cps, true);   // two recurrences
-  const size_t part = align256((size_t)2 * d->B * d->T * d->H * DK * sizeof(float));
+  const size_t part = align256((size_t)d->B * d->T * d->H * DK * sizeof(float));
+  const size_t tok = align256((size_t)d->B * d->T * d->H * sizeof(float));
   size_t off = 0;
   p.off_dq = off; off += part;
   p.off_dk = off; off += part;
+  p.off_rq = off; off += tok;
+  p.off_rk = off; off += tok;
   p.off_st = off; off += align256((size_t)BH * kStateElems * sizeof(float));
   p.off_r = off; off += align256((size_t)BH * p.sp.n_chunks * sizeof(float));
   const size_t seg = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * kStateElems * sizeof(float)) : 0;
@@ -446,25 +468,21 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   hipStream_t st = (hipStream_t)stream;
   float* dq_part = (float*)(w + p.off_dq);
   float* dk_part = (float*)(w + p.off_dk);
+  float* rq = (float*)(w + p.off_rq);
+  float* rk = (float*)(w + p.off_rk);
   float* S_T = (float*)(w + p.off_st);
   float* seg_f = sp.nseg > 1 ? (float*)(w + p.off_segf) : nullptr;
   float* seg_r = sp.nseg > 1 ? (float*)(w + p.off_segr) : nullptr;
-  const int64_t plane = dims->B * dims->T * dims->H * DK;   // between the two partial sums
-  // fp32 partial-sum outputs [2][B,T,H,DK], one plane per dv-half
-  auto part_view = [&](float* base, bool backwards) {
-    TokView v = tok_view(base, 4, dims, DK, 0, backwards);
-    v.ss = plane;
-    return v;
-  };
 
   // 1. dq.  Forward recurrence with keys = a dv-half of v, values = k (its
   //    state is the half of S^T), queries = the same half of dO; the two
-  //    halves give partial sums of dq.  Also S_T when dS_T is given.
+  //    halves are sums over the two halves of the value width.  Also S_T when
+  //    dS_T is given.
   WalkArgs f{};
   f.X = tok_view(v, 2, dims, DV, hw, false);
   f.Y = tok_view(k, 2, dims, DK, 0, false);
   f.Q = tok_view(dO, 2, dims, DV, hw, false);
-  f.O = part_view(dq_part, false);
+  f.O = tok_view(dq_part, 4, dims, DK, 0, false);
   f.g = g;
   f.gsb = dims->T * dims->H;
   f.gsh = 1;
@@ -508,43 +526,62 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
     fseg = coarse(fseg, sp);
     rseg = coarse(rseg, sp);
   }
-  e = walk_segments(f, WV_FWD_OUT_BF16_F32, sp, fseg, ffin, BH, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq walk");
   // 2a. dv: queries k, outputs dv (a dv-half per slice); the final state is
   //     the gradient leaving the first token (dS0 after its decay, below).
   WalkArgs rv = r;
   rv.Q = tok_view(k, 2, dims, DK, 0, true);
   rv.O = tok_view(dv, osz, dims, DV, hw, true);
-  e = walk_segments(rv, out_variant, sp, rseg, state_plain(dS0, hw), BH, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dv walk");
   // 2b. dk: keys a dv-half of dO, values q (the state is the transpose),
-  //     queries the same half of v; partial sums of dk.
-  WalkArgs rk = r;
-  rk.X = tok_view(dO, 2, dims, DV, hw, true);
-  rk.Y = tok_view(q, 2, dims, DK, 0, true);
-  rk.Q = tok_view(v, 2, dims, DV, hw, true);
-  rk.O = part_view(dk_part, true);
+  //     queries the same half of v.
+  WalkArgs rk_ = r;
+  rk_.X = tok_view(dO, 2, dims, DV, hw, true);
+  rk_.Y = tok_view(q, 2, dims, DK, 0, true);
+  rk_.Q = tok_view(v, 2, dims, DV, hw, true);
+  rk_.O = tok_view(dk_part, 4, dims, DK, 0, true);
   StateView rkseg = rseg;
   rkseg.sx = rseg.sy;
   rkseg.sy = rseg.sx;
-  e = walk_segments(rk, WV_FWD_OUT_BF16_F32, sp, rkseg, StateView{}, BH, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dk walk");
 
-  // 3. dq, dk from the partial sums; q.dq - k.dk and its in-chunk suffix sums
+  // dq and dk run as one walk per dv-half.  The first half writes fp32 sums;
+  // the second adds them to its own (a fixed order), writes the gradient and
+  // its dot product with q (k) for the log-decay gradient.
+  SegPlan sp1 = sp;
+  sp1.ns = 1;
+  auto half = [&](WalkArgs a, int hh) {
+    a.X = shifted(a.X, (int64_t)hh * hw, 2);
+    a.Q = shifted(a.Q, (int64_t)hh * hw, 2);
+    return a;
+  };
+  WalkArgs q0 = segments_args(half(f, 0), sp1, fseg, ffin);
+  WalkArgs k0 = segments_args(half(rk_, 0), sp1, rkseg, StateView{});
+  WalkArgs q1 = segments_args(half(f, 1), sp1, shifted(fseg, hw), shifted(ffin, hw));
+  WalkArgs k1 = segments_args(half(rk_, 1), sp1, shifted(rkseg, hw), StateView{});
+  q1.acc = q0.O;
+  q1.O = tok_view(dq, osz, dims, DK, 0, false);
+  q1.D = tok_view(q, 2, dims, DK, 0, false);
+  q1.rdot = token_floats(rq, dims, false);
+  k1.acc = k0.O;
+  k1.O = tok_view(dk, osz, dims, DK, 0, true);
+  k1.D = tok_view(k, 2, dims, DK, 0, true);
+  k1.rdot = token_floats(rk, dims, true);
+  const int nw = (int)(BH * sp1.nseg);
+  e = launch_out_walk_pair(q0, nw, k0, nw, 0, st);
+  if (e == hipSuccess) e = launch_out_walk_pair(q1, nw, k1, nw, dims->out_dtype == GLA_BF16, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq/dk walks");
+  e = walk_segments(rv, out_variant, sp, rseg, state_plain(dS0, hw), BH, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dv walk");
+
+  // 3. q.dq - k.dk and its in-chunk suffix sums
   BwdFinishArgs fa{};
-  fa.q = q;
-  fa.k = k;
-  fa.dq_part = dq_part;
-  fa.dk_part = dk_part;
-  fa.dq = dq;
-  fa.dk = dk;
+  fa.rq = rq;
+  fa.rk = rk;
   fa.dg = dg;
   fa.chunk_r = (float*)(w + p.off_r);
   fa.B = dims->B;
   fa.T = dims->T;
   fa.H = dims->H;
   fa.n_chunks = sp.n_chunks;
-  e = launch_bwd_finish(fa, dims->out_dtype == GLA_BF16, st);
+  e = launch_bwd_finish(fa, st);
   if (e != hipSuccess) return device_err(e, "gla_chunk_bwd finish");
   // 4. d-log-decay: add later chunks and <dS_T, S_T>; dS0 through the first decay
   e = launch_dg_finish(dg, fa.chunk_r, dS_T, S_T, dS0, g, dims->B, dims->T, dims->H, sp.n_chunks, st);

@@ -8,7 +8,8 @@
 //   dv_t = sum_{s>=t} e^{b_s-b_t} (k_t.q_s) dO_s + ...      backward in time,
 //   dk_t = sum_{s>=t} e^{b_s-b_t} (v_t.dO_s) q_s + ...      backward in time,
 // where the contraction over the 192 value columns (dq, dk) is split into two
-// halves whose fp32 partial sums are added here.  The log-decay gradient uses
+// halves: the walk of the second half adds the first half's fp32 partial sums
+// and writes q_t.dq_t (k_t.dk_t).  The log-decay gradient uses
 //     dg_t = sum_{u >= t} (q_u.dq_u - k_u.dk_u) + <dS_T, S_T>
 // (derivative through the running sum of the log-decay): bwd_finish writes
 // the in-chunk suffix sums and the chunk totals, dg_finish adds the rest.
@@ -17,63 +18,27 @@
 
 namespace gla {
 
-// One workgroup per (batch, head, chunk).  Threads walk the chunk's 128 x 96
-// gradient rows as 16-byte pieces of 8 columns (row-contiguous accesses).
-template <class TOut>
+// r_t = q_t.dq_t - k_t.dk_t (both dot products written by the last walks of
+// dq and dk), its in-chunk suffix sums into dg and the chunk totals.  One
+// wave per (batch, head, chunk), four per workgroup; two tokens per lane.
 __global__ void __launch_bounds__(256) bwd_finish_kernel(BwdFinishArgs a) {
-  __shared__ float part[CH][13];            // per token: r of each 8-column piece
   const int N = a.n_chunks;
-  const int64_t item = blockIdx.x;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.B * a.H * N) return;
   const int n = (int)(item % N);
   const int64_t bh = item / N;
   const int h = (int)(bh % a.H);
   const int64_t b = bh / a.H;
   const int64_t T = a.T;
-  const int64_t plane = a.B * T * a.H * DK;   // distance between the two partial sums
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int p = threadIdx.x + 256 * i, row = p / 12, cp = p % 12;
-    const int64_t t = (int64_t)n * CH + row;
-    float r = 0.f;
-    if (t < T) {
-      const int64_t off = ((b * T + t) * a.H + h) * DK + cp * 8;
-      const f32x4 qa = *(const f32x4*)(a.dq_part + off), qb = *(const f32x4*)(a.dq_part + off + 4);
-      const f32x4 qc = *(const f32x4*)(a.dq_part + plane + off), qd = *(const f32x4*)(a.dq_part + plane + off + 4);
-      const f32x4 ka = *(const f32x4*)(a.dk_part + off), kb = *(const f32x4*)(a.dk_part + off + 4);
-      const f32x4 kc = *(const f32x4*)(a.dk_part + plane + off), kd = *(const f32x4*)(a.dk_part + plane + off + 4);
-      const bf16x8 qv = *(const bf16x8*)((const bf16*)a.q + off);
-      const bf16x8 kv = *(const bf16x8*)((const bf16*)a.k + off);
-      const f32x4 dq0 = qa + qc, dq1 = qb + qd, dk0 = ka + kc, dk1 = kb + kd;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r += (float)qv[e] * dq0[e] - (float)kv[e] * dk0[e];
-        r += (float)qv[e + 4] * dq1[e] - (float)kv[e + 4] * dk1[e];
-      }
-      store4((TOut*)a.dq + off, dq0);
-      store4((TOut*)a.dq + off + 4, dq1);
-      store4((TOut*)a.dk + off, dk0);
-      store4((TOut*)a.dk + off + 4, dk1);
-    }
-    part[row][cp] = r;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    // r of tokens 2l, 2l+1 (pieces summed in a fixed order), then in-chunk
-    // suffix sums
-    const int l = threadIdx.x;
-    float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-    for (int cp = 0; cp < 12; ++cp) {
-      r0 += part[2 * l][cp];
-      r1 += part[2 * l + 1][cp];
-    }
-    const float suf = wave_incl_rscan(r0 + r1);     // sum over tokens >= 2l
-    float* dgb = a.dg + b * T * a.H + h;
-    const int64_t ta = (int64_t)n * CH + 2 * l, tb = ta + 1;
-    if (ta < T) dgb[ta * a.H] = suf;
-    if (tb < T) dgb[tb * a.H] = suf - r0;
-    if (l == 0) a.chunk_r[bh * N + n] = suf;
-  }
+  const int l = threadIdx.x & 63;
+  const int64_t ta = (int64_t)n * CH + 2 * l, tb = ta + 1;
+  const int64_t base = b * T * a.H + h;
+  const float r0 = ta < T ? a.rq[base + ta * a.H] - a.rk[base + ta * a.H] : 0.f;
+  const float r1 = tb < T ? a.rq[base + tb * a.H] - a.rk[base + tb * a.H] : 0.f;
+  const float suf = wave_incl_rscan(r0 + r1);     // sum over tokens >= 2l
+  if (ta < T) a.dg[base + ta * a.H] = suf;
+  if (tb < T) a.dg[base + tb * a.H] = suf - r0;
+  if (l == 0) a.chunk_r[bh * N + n] = suf;
 }
 
 // dg += (sum of the chunk totals after this chunk) + <dS_T, S_T>, and
@@ -118,10 +83,9 @@ __global__ void __launch_bounds__(256) dg_finish_kernel(float* dg, const float* 
   }
 }
 
-hipError_t launch_bwd_finish(const BwdFinishArgs& a, int out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)(a.B * a.H * a.n_chunks)), block(256);
-  if (out_bf16) hipLaunchKernelGGL((bwd_finish_kernel<bf16>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_finish_kernel<float>), grid, block, 0, st, a);
+hipError_t launch_bwd_finish(const BwdFinishArgs& a, hipStream_t st) {
+  const int64_t items = a.B * a.H * a.n_chunks;
+  hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -48,6 +48,9 @@ struct WalkArgs {
   const float* g;       // log-decay of walk token t: g[b*gsb + h*gsh + (t - gshift)*gst],
   int64_t gsb, gsh, gst;  // zero for t < gshift
   int gshift;
+  TokView acc;          // with output: fp32 partial sums added to the outputs (p null: none)
+  TokView D;            // with acc: rows dotted with the final outputs (bf16, width of Y)
+  TokView rdot;         // with acc: those dot products, one float per token (p null: none)
   StateView zinit;      // initial state (p null: zero)
   StateView zfin;       // final state (p null: not written)
   int zfin_only_seg;    // -1: every segment writes; else only that segment
@@ -60,6 +63,9 @@ struct WalkArgs {
 hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st);
 // Two independent bf16 state-only walks in one launch (nwg0 + nwg1
 // workgroups).
+// Two bf16 walks with output in one launch (nwg0 + nwg1 workgroups).
+hipError_t launch_out_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, int out_bf16,
+                                hipStream_t st);
 hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st);
 int walk_slices(int variant);
 hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, int64_t BH, int nseg, int rev,
@@ -75,15 +81,13 @@ hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, hipStream_t
 
 // Backward finish: see gla_bwd.hip.
 struct BwdFinishArgs {
-  const void* q; const void* k;       // [B,T,H,DK] bf16
-  const float* dq_part;               // [2][B,T,H,DK] fp32 partial sums of dq
-  const float* dk_part;               // [2][B,T,H,DK] fp32 partial sums of dk
-  void* dq; void* dk;                 // [B,T,H,DK] results
-  float* dg;                          // [B,T,H] in-chunk suffix sums of q.dq - k.dk
+  const float* rq;                    // [B,T,H] q_t.dq_t
+  const float* rk;                    // [B,T,H] k_t.dk_t
+  float* dg;                          // [B,T,H] in-chunk suffix sums of rq - rk
   float* chunk_r;                     // [BH][N] per-chunk totals
   int64_t B, T; int H, n_chunks;
 };
-hipError_t launch_bwd_finish(const BwdFinishArgs& a, int out_bf16, hipStream_t st);
+hipError_t launch_bwd_finish(const BwdFinishArgs& a, hipStream_t st);
 hipError_t launch_dg_finish(float* dg, const float* chunk_r, const float* dS_T, const float* S_T, float* dS0,
                             const float* g, int64_t B, int64_t T, int H, int n_chunks, hipStream_t st);
 

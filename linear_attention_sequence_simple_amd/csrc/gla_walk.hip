@@ -850,6 +850,37 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
           o[cb] = mfma(yv[bf][cb], pl[J][s], o[cb]);
         }
       }
+      if (a.acc.p) {
+        // Add a partial sum of the same outputs (fp32, computed by another
+        // walk over the other half of a contraction) and, when asked, write
+        // the dot product of each output row with a row of D.
+        const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
+        const bool live = trow < T;
+        const float* ap = (const float*)a.acc.p + b * a.acc.sb + h * a.acc.sh + trow * a.acc.st + 4 * g2;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 v = live ? load4f(ap + 32 * cb + 8 * qq) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] += v[e];
+          }
+        if (a.rdot.p) {
+          const bf16* dp = (const bf16*)a.D.p + b * a.D.sb + h * a.D.sh + trow * a.D.st + 4 * g2;
+          float r = 0.f;
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const bf16x4 dv = live ? *(const bf16x4*)(dp + 32 * cb + 8 * qq) : bf16x4{};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) r += (float)dv[e] * o[cb][4 * qq + e];
+            }
+          r += __shfl_xor(r, 32, 64);
+          if (g2 == 0 && live)
+            ((float*)a.rdot.p)[b * a.rdot.sb + h * a.rdot.sh + trow * a.rdot.st] = r;
+        }
+      }
       if constexpr (std::is_same<TOut, bf16>::value) {
         // Through this wave's own rows of the query tile (free until the
         // next phase 1; the wave's LDS accesses execute in order): written
@@ -1057,6 +1088,24 @@ hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st) 
     case WV_FWD_STATE_F32: return launch_one<float, float, 2, WALK_FWD_STATE>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <class TOut>
+__global__ void __launch_bounds__(WalkShape<WALK_FWD_OUT>::THREADS, 1)
+    walk_out_pair_kernel(WalkArgs a0, WalkArgs a1, int nwg0) {
+  __shared__ WalkSmem<bf16, 3, true> sm;
+  if ((int)blockIdx.x < nwg0)
+    walk_block<bf16, TOut, 3, WALK_FWD_OUT>(a0, sm, (int)blockIdx.x, nwg0);
+  else
+    walk_block<bf16, TOut, 3, WALK_FWD_OUT>(a1, sm, (int)blockIdx.x - nwg0, (int)gridDim.x - nwg0);
+}
+
+hipError_t launch_out_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, int out_bf16,
+                                hipStream_t st) {
+  const dim3 grid(nwg0 + nwg1), block(WalkShape<WALK_FWD_OUT>::THREADS);
+  if (out_bf16) hipLaunchKernelGGL((walk_out_pair_kernel<bf16>), grid, block, 0, st, a0, a1, nwg0);
+  else hipLaunchKernelGGL((walk_out_pair_kernel<float>), grid, block, 0, st, a0, a1, nwg0);
+  return hipGetLastError();
 }
 
 hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st) {
