@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close, inputs, rel_err, to_dev, to_np
+from gpu_util import assert_close, assert_close_bf16_out, inputs, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def check(d, got, S0=True, dS_T=True):
         assert_close(got[4], ref[4], TOL, "dS0")
 
 
-@pytest.mark.parametrize("T", [128, 200, 300, 513])
+@pytest.mark.parametrize("T", [1, 77, 128, 200, 300, 513])
 @pytest.mark.parametrize("s0,dst", [(True, True), (False, False)])
 def test_reduced(T, s0, dst):
     d = inputs("bwd_bf16_b4_t4096", seed=T, B=2, T=T, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
@@ -74,6 +74,18 @@ def test_segments(T, segments):
     d = inputs("bwd_bf16_b4_t4096", seed=6, B=1, T=T, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
     got = run_bwd(d, segments=segments)
     check(d, got)
+
+
+def test_bf16_gradients():
+    # gradients written in bf16: elementwise bound of the rounding on top of
+    # the tolerance; dg stays fp32
+    d = inputs("bwd_bf16_b4_t4096", seed=9, B=2, T=333, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
+    got = run_bwd(d, out_dtype=torch.bfloat16)
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], d["S0"], d["dS_T"])
+    for name, x, y in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close_bf16_out(x, y, TOL, name + "(bf16)")
+    assert_close(got[3], ref[3], TOL, "dg")
+    assert_close(got[4], ref[4], TOL, "dS0")
 
 
 def test_backward_workload_sampled():
