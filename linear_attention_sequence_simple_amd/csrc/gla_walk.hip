@@ -194,6 +194,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   constexpr bool COMP = S::COMP;
   constexpr int NTHR = 256;                           // loader threads: the 4 state waves
   constexpr bool LOADER = !OUTW;
+  static_assert(!(OUT && COMP), "the bf16 walks with output run prefill_wave");
 
   const int lane = lane_id();
   const int g2 = lane >> 5;
@@ -241,29 +242,14 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   constexpr int DEPTH = (!OUT && COMP) ? 2 : 1;
   TileRegs<TIn, DK, NTHR> px[DEPTH];
   TileRegs<TIn, DVS, NTHR> py[DEPTH];
-  TileRegs<TIn, (OUT && !COMP) ? DK : 8, NTHR> pq[DEPTH];
-  // bf16 queries of this output wave's 32 tokens, as plain-order MFMA B
-  // operands: the current chunk's and, in flight, the next chunk's
-  bf16x8 qcur[(OUTW && COMP) ? 3 : 1][2], qnxt[(OUTW && COMP) ? 3 : 1][2];
+  TileRegs<TIn, OUT ? DK : 8, NTHR> pq[DEPTH];
   auto prefetch = [&](auto bc, int n) {
     constexpr int B = decltype(bc)::value % DEPTH;
     const int t0 = n * CH;
     if constexpr (LOADER) {
       px[B].load(Xb, a.X.st, t0, T);
       py[B].load(Yb, a.Y.st, t0, T);
-      if constexpr (OUT && !COMP) pq[B].load(Qb, a.Q.st, t0, T);
-    }
-  };
-  auto prefetch_q = [&](int n) {
-    const int t0 = n * CH;
-    if constexpr (OUTW && COMP) {
-      const int64_t t = t0 + 32 * W + (lane & 31);
-      const bf16* qr = (const bf16*)Qb + t * a.Q.st + 8 * g2;
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          qnxt[kb][s] = t < T ? *(const bf16x8*)(qr + 32 * kb + 16 * s) : bf16x8{};
+      if constexpr (OUT) pq[B].load(Qb, a.Q.st, t0, T);
     }
   };
   constexpr std::integral_constant<int, 0> I0{};
@@ -285,7 +271,6 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   auto step_of = [&](int i) { return n_begin + i; };
   if (nloc > 0) {
     prefetch(I0, step_of(0));
-    prefetch_q(step_of(0));
     if (DEPTH == 2 && nloc > 1) prefetch(I1, step_of(1));
     load_g(step_of(0));
     if (W == 0) build_decay(&sm.dec[0], gx0, gx1, gm0, gm1, OUT ? sm.utab[0] : nullptr);
@@ -303,17 +288,12 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     if constexpr (LOADER) {
       if constexpr (S::RAWX) px[B].template store<S::PX>(sm.x);
       py[B].template store<S::PY>(sm.y);
-      if constexpr (OUT && !COMP) pq[B].template store<S::PQ>(sm.q);
+      if constexpr (OUT) pq[B].template store<S::PQ>(sm.q);
       if constexpr (COMP)
         px[B].template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, dc.kap);
     }
     // chunk it+DEPTH goes into this buffer now that it is staged
     if (it + DEPTH < nloc) prefetch(bc, step_of(it + DEPTH));
-    if constexpr (OUTW && COMP) {
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb) { qcur[kb][0] = qnxt[kb][0]; qcur[kb][1] = qnxt[kb][1]; }
-    }
-    if (it + 1 < nloc) prefetch_q(step_of(it + 1));
     if constexpr (OUT) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -322,12 +302,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const f32x4 v4 = f32x4{z[t][4 * qq], z[t][4 * qq + 1], z[t][4 * qq + 2], z[t][4 * qq + 3]};
-          if constexpr (COMP) {
-            const int off = swz96(d, 32 * cb + 8 * qq + 4 * g2);
-            store4_split((bf16*)sm.z + off, (bf16*)sm.zl + off, v4);
-          } else {
-            store4(sm.z + d * S::PZ + 32 * cb + 8 * qq + 4 * g2, v4);
-          }
+          store4(sm.z + d * S::PZ + 32 * cb + 8 * qq + 4 * g2, v4);
         }
       }
     }
@@ -342,42 +317,21 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 #pragma unroll
       for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-          if constexpr (COMP) qn[kb][s] = qcur[kb][s];
-          else qn[kb][s] = frag_kcP(sm.q, S::PQ, 32 * W, 32 * kb, s);
-        }
+        for (int s = 0; s < SUB; ++s) qn[kb][s] = frag_kcP(sm.q, S::PQ, 32 * W, 32 * kb, s);
       // Decay-masked scores P^T (keys j in rows, queries i in columns), all
       // key blocks at once.  Off the diagonal 2^{b_i - b_j} =
       // 2^{b_i - b_{32W}} 2^{b_{32W} - b_j}, both factors <= 1.
       f32x16 acc[W + 1];
 #pragma unroll
       for (int J = 0; J <= W; ++J) acc[J] = f32x16{};
-      if constexpr (COMP) {
-        bf16x8 xk[2][W + 1];
 #pragma unroll
-        for (int J = 0; J <= W; ++J) xk[0][J] = sfrag_kcN((const bf16*)sm.x, 32 * J, 0, 0);
+      for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
-        for (int k = 0; k < 6; ++k) {
-          const int cur = k & 1, kb = k >> 1, s = k & 1;
-          if (k + 1 < 6) {
+        for (int s = 0; s < SUB; ++s)
 #pragma unroll
-            for (int J = 0; J <= W; ++J)
-              xk[cur ^ 1][J] = sfrag_kcN((const bf16*)sm.x, 32 * J, 32 * ((k + 1) >> 1), (k + 1) & 1);
-          }
-#pragma unroll
-          for (int J = 0; J <= W; ++J) acc[J] = mfma(xk[cur][J], qn[kb][s], acc[J]);
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-          for (int s = 0; s < SUB; ++s)
-#pragma unroll
-            for (int J = 0; J <= W; ++J)
-              acc[J] = mfma(frag_kcP(sm.x, S::PX, 32 * J, 32 * kb, s), qn[kb][s], acc[J]);
-      }
+          for (int J = 0; J <= W; ++J)
+            acc[J] = mfma(frag_kcP(sm.x, S::PX, 32 * J, 32 * kb, s), qn[kb][s], acc[J]);
       FT pf[W + 1][SUB];
-      FT pl[COMP ? W + 1 : 1][SUB];
       const float ri = W > 0 ? exp2f(bi - dc.b2[32 * W]) : 1.f;
 #pragma unroll
       for (int J = 0; J <= W; ++J) {
@@ -398,80 +352,29 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
           }
         }
 #pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-          if constexpr (COMP) split_tile(acc[J], s, pf[J][s], pl[J][s]);
-          else pf[J][s] = acc[J][s];
-        }
+        for (int s = 0; s < SUB; ++s) pf[J][s] = acc[J][s];
       }
       // Outputs of all dv blocks at once: O^T = diag(Lambda) (Z^T Q^T) + V^T P^T.
       f32x16 o[NC];
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) o[cb] = f32x16{};
-      if constexpr (COMP) {
-        // Software-pipelined: the operands of step k+1 are requested before
-        // the MFMAs of step k, so LDS latency overlaps matrix-core work.
-        bf16x8 zh[2][NC], zlo[2][NC];
 #pragma unroll
-        for (int cb = 0; cb < NC; ++cb) {
-          zh[0][cb] = sfrag_krN((const bf16*)sm.z, 0, 32 * cb, 0);
-          zlo[0][cb] = sfrag_krN((const bf16*)sm.zl, 0, 32 * cb, 0);
-        }
+      for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
-        for (int k = 0; k < 6; ++k) {
-          const int cur = k & 1, kb = k >> 1, s = k & 1;
-          if (k + 1 < 6) {
+        for (int s = 0; s < SUB; ++s)
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb) {
-              zh[cur ^ 1][cb] = sfrag_krN((const bf16*)sm.z, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
-              zlo[cur ^ 1][cb] = sfrag_krN((const bf16*)sm.zl, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
-            }
-          }
-#pragma unroll
-          for (int cb = 0; cb < NC; ++cb) {
-            o[cb] = mfma(zh[cur][cb], qn[kb][s], o[cb]);
-            o[cb] = mfma(zlo[cur][cb], qn[kb][s], o[cb]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-          for (int s = 0; s < SUB; ++s)
-#pragma unroll
-            for (int cb = 0; cb < NC; ++cb)
-              o[cb] = mfma(frag_kr(sm.z, S::PZ, 32 * kb, 32 * cb, s), qn[kb][s], o[cb]);
-      }
+          for (int cb = 0; cb < NC; ++cb)
+            o[cb] = mfma(frag_kr(sm.z, S::PZ, 32 * kb, 32 * cb, s), qn[kb][s], o[cb]);
       const float lam = exp2f(dc.b2[il]);
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) o[cb] *= lam;
-      if constexpr (COMP) {
-        constexpr int NK = 2 * (W + 1);                 // (J, s) steps
-        bf16x8 yv[2][NC];
 #pragma unroll
-        for (int cb = 0; cb < NC; ++cb) yv[0][cb] = sfrag_kr((const bf16*)sm.y, 0, 32 * cb, 0);
+      for (int J = 0; J <= W; ++J)
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-          const int cur = k & 1, J = k >> 1, s = k & 1;
-          if (k + 1 < NK) {
+        for (int s = 0; s < SUB; ++s)
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb)
-              yv[cur ^ 1][cb] = sfrag_kr((const bf16*)sm.y, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
-          }
-#pragma unroll
-          for (int cb = 0; cb < NC; ++cb) {
-            o[cb] = mfma(yv[cur][cb], pf[J][s], o[cb]);
-            o[cb] = mfma(yv[cur][cb], pl[J][s], o[cb]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int J = 0; J <= W; ++J)
-#pragma unroll
-          for (int s = 0; s < SUB; ++s)
-#pragma unroll
-            for (int cb = 0; cb < NC; ++cb)
-              o[cb] = mfma(frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s), pf[J][s], o[cb]);
-      }
+          for (int cb = 0; cb < NC; ++cb)
+            o[cb] = mfma(frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s), pf[J][s], o[cb]);
       const int64_t trow = (int64_t)n * CH + il;
       if (trow < T) {
         TOut* op = (TOut*)a.O.p + b * a.O.sb + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
