@@ -23,11 +23,11 @@ import numpy as np
 __all__ = [
     "WORKLOADS", "TENSOR_IDS", "rng", "bf16_round", "bf16_bits",
     "logsigmoid", "make_g", "make_inputs", "make_decode_step",
-    "make_decode_state",
+    "make_decode_state", "make_packed_inputs",
 ]
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "g": 3, "S0": 4, "dO": 5, "u_head": 6,
-              "dS_T": 7, "slot": 8}
+              "dS_T": 7, "slot": 8, "len": 9}
 
 # name -> description.  "g" names the log-decay recipe (see make_g),
 # "S0" the initial-state recipe ("zero" or "normal0.1": N(0, 0.1^2)).
@@ -43,6 +43,12 @@ WORKLOADS = {
                               S0="normal0.1"),
     "bwd_bf16_b4_t4096": dict(id=5, kind="bwd", B=4, T=4096, H=16, dk=96, dv=192,
                               dtype="bf16", g="logsig_n4", S0="zero"),
+    # serving prefill: prompts of 2,048 to 8,192 tokens ("I risultati dichiarati
+    # hanno limiti precisi") packed into one batch, states in a pool of 1,280
+    # slots ("Resultados de entrenamiento e inferencia")
+    "serve_prefill_16x2k8k": dict(id=6, kind="packed", n_seq=16, len_lo=2048,
+                                  len_hi=8192, n_slots=1280, H=16, dk=96, dv=192,
+                                  dtype="bf16", g="logsig_n4", S0="normal0.1"),
 }
 
 
@@ -157,4 +163,49 @@ def make_decode_step(n_seq: int, step: int, H=16, dk=96, dv=192, seed=0,
     if dtype == "bf16":
         for key in ("q", "k", "v"):
             out[key] = bf16_round(out[key])
+    return out
+
+
+def make_packed_inputs(workload: str = "serve_prefill_16x2k8k", seed: int = 0, lengths=None,
+                       n_slots=None, H=None, dtype=None, g=None, with_pool=True) -> dict:
+    """Sequences of different lengths packed along one token axis.
+
+    lengths    : per-sequence token counts (default: n_seq draws, uniform
+                 integers in [len_lo, len_hi])
+    returns q, k [N, H, dk], v [N, H, dv], g [N, H] (float32 arrays, bf16
+    values for bf16 workloads), cu_seqlens int32 [n_seq + 1], slot_idx int32
+    [n_seq] (distinct slots of an n_slots pool, in random order) and, with
+    with_pool, the pool's initial states float32 [n_slots, H, dk, dv] drawn
+    N(0, 0.1^2).
+    """
+    w = dict(WORKLOADS[workload])
+    for key, val in (("n_slots", n_slots), ("H", H), ("dtype", dtype), ("g", g)):
+        if val is not None:
+            w[key] = val
+    wid, Hn, K, V = w["id"], w["H"], w["dk"], w["dv"]
+    if lengths is None:
+        lengths = rng(wid, "len", seed).integers(w["len_lo"], w["len_hi"] + 1, size=w["n_seq"])
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n_seq = len(lengths)
+    if n_seq > w["n_slots"]:
+        raise ValueError(f"{n_seq} sequences do not fit {w['n_slots']} slots")
+    cu = np.zeros(n_seq + 1, np.int64)
+    cu[1:] = np.cumsum(lengths)
+    N = int(cu[-1])
+    sc = 1.0 / math.sqrt(K)
+    out = {
+        "q": _normal(wid, "q", seed, (N, Hn, K), sc),
+        "k": _normal(wid, "k", seed, (N, Hn, K), sc),
+        "v": _normal(wid, "v", seed, (N, Hn, V), sc),
+        "g": make_g(w["g"], (N, Hn), wid, seed),
+        "cu_seqlens": cu.astype(np.int32),
+        "slot_idx": rng(wid, "slot", seed).permutation(w["n_slots"])[:n_seq].astype(np.int32),
+    }
+    if with_pool:
+        out["pool"] = _normal(wid, "S0", seed, (w["n_slots"], Hn, K, V), 0.1)
+    if w["dtype"] == "bf16":
+        for key in ("q", "k", "v"):
+            out[key] = bf16_round(out[key])
+    w["lengths"] = lengths
+    out["meta"] = w
     return out

@@ -128,6 +128,45 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k,
                          float* S_T, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Prefill of a batch of sequences of different lengths, packed along one
+ * token axis, with the states kept in a pool slot per sequence: the serving
+ * layout in which a wrapper ties each sequence's recurrent state to the
+ * engine's memory pool and prompts of different lengths share a batch ("AWS
+ * serve Laplace 3B di i14 con uno stato fisso di 29,5 MB", sections "Lo stato
+ * di Laplace 3B resta fisso durante l'inferenza" and "I risultati dichiarati
+ * hanno limiti precisi").  Each sequence is an independent gla_chunk_fwd.
+ *
+ *   dims        : B = number of sequences, T = an upper bound of every
+ *                 sequence's length (it sizes the launch plan and the
+ *                 workspace), H, dk, dv, chunk and dtypes as for gla_chunk_fwd
+ *   total_tokens: rows of the packed tensors, < 2^31
+ *   cu_seqlens  : device int32 [B + 1]; sequence b is rows
+ *                 [cu_seqlens[b], cu_seqlens[b+1]).  Non-decreasing, within
+ *                 [0, total_tokens], lengths <= T (caller contract: the
+ *                 kernels clamp offsets into [0, total_tokens] and lengths to
+ *                 [0, T], so no access leaves the tensors).  Empty sequences
+ *                 are allowed: their slot keeps (or is set to) the initial
+ *                 state.
+ *   q, k : [total_tokens, H, dk] in_dtype   v : [total_tokens, H, dv] in_dtype
+ *   g    : [total_tokens, H] float32        o : [total_tokens, H, dv] out_dtype
+ *   pool, slot_idx : sequence b uses slot slot_idx[b] (device int32 [B]) or
+ *                 slot b when slot_idx is NULL; indices in range and
+ *                 distinct (caller contract, not checked on the device).
+ *   init_from_pool : 1 = start from the slot's state (a prompt continued),
+ *                 0 = start from zero (a new prompt).
+ *   The final state of every sequence is written to its slot.
+ *   ws   : at least gla_workspace_size(GLA_OP_FWD, dims) bytes.
+ * Errors: as gla_chunk_fwd, plus INVALID_ARGUMENT for a NULL or misaligned
+ * cu_seqlens, a pool whose H/dk/dv differ, B > slots with slot_idx NULL.
+ */
+gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens,
+                                const int32_t* cu_seqlens, const void* q,
+                                const void* k, const void* v, const float* g,
+                                gla_state* pool, const int32_t* slot_idx,
+                                int32_t init_from_pool, void* o, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Batched single-token decode step, in place on a state pool.  For each of B
  * sequences and each head: S <- exp(g) S + k^T v, then o = q S.  The state
  * stays float32 and the cost per token does not depend on the context length

@@ -5,6 +5,9 @@ stream, every step of the computation runs in the library's kernels.  The
 functions carry the names of the C entry points (include/gla.h):
 
     gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None)        -> (o, S_T)
+    gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool,
+                         slot_idx=None, init_from_pool=False,
+                         out_dtype=None)                       -> o
     gla_recurrent_step(pool, q, k, v, g, slot_idx=None, out_dtype=None) -> o
     gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None,
                   want_dS0=False)                             -> (dq, dk, dv, dg, dS0)
@@ -12,7 +15,8 @@ functions carry the names of the C entry points (include/gla.h):
     gla_workspace_size(op, dims)                              -> int
 
 Layouts: q, k [B,T,H,96]; v, o, dO [B,T,H,192]; g [B,T,H] float32; states
-[B,H,96,192] float32.  There is no fallback: without the built library on a
+[B,H,96,192] float32; packed sequences [N,H,...] with int32 offsets
+cu_seqlens [n_seq+1] and their states in a StatePool.  There is no fallback: without the built library on a
 GPU every call raises.
 """
 from __future__ import annotations
@@ -23,7 +27,7 @@ import os
 import torch
 
 __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDims",
-           "lib", "lib_path", "gla_chunk_fwd", "gla_recurrent_step", "gla_chunk_bwd",
+           "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS"]
 
 GLA_F32, GLA_BF16 = 0, 1
@@ -33,7 +37,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_INVALID_ARGUMENT", 2: "GLA_ERR_UNSUPPORTED",
           3: "GLA_ERR_OUT_OF_MEMORY", 4: "GLA_ERR_DEVICE"}
 EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slots",
            "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
-           "gla_recurrent_step", "gla_chunk_bwd", "gla_status_str", "gla_last_error"]
+           "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd", "gla_status_str",
+           "gla_last_error"]
 
 
 class GlaError(RuntimeError):
@@ -76,13 +81,14 @@ def lib():
     L.gla_state_slot_bytes.restype = SZ
     L.gla_workspace_size.argtypes = [I32, ctypes.POINTER(GlaDims), ctypes.POINTER(SZ)]
     L.gla_chunk_fwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, SZ, P]
+    L.gla_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GlaDims), I64, P, P, P, P, P, P, P, I32, P, P, SZ, P]
     L.gla_recurrent_step.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
     L.gla_chunk_bwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.gla_status_str.argtypes = [I32]
     L.gla_status_str.restype = ctypes.c_char_p
     L.gla_last_error.restype = ctypes.c_char_p
     for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd",
-                 "gla_recurrent_step", "gla_chunk_bwd"):
+                 "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd"):
         getattr(L, name).restype = I32
     _LIB = L
     return L
@@ -170,6 +176,43 @@ def gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspac
     _check(lib().gla_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
                                _ptr(o), _ptr(S_T), _ptr(ws), nbytes, _stream()))
     return o, S_T
+
+
+def gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool, slot_idx=None,
+                         init_from_pool=False, out_dtype=None, workspace=None, o=None):
+    """Prefill of packed sequences of different lengths into pool slots.
+
+    q, k [N,H,96]; v [N,H,192]; g [N,H] float32; cu_seqlens int32 [n_seq+1]
+    on the device (sequence b is rows cu_seqlens[b]:cu_seqlens[b+1]);
+    max_seqlen bounds every sequence's length; pool a StatePool; slot_idx
+    int32 [n_seq] on the device or None (sequence b uses slot b).  Each
+    sequence starts from its slot's state (init_from_pool) or from zero, and
+    its final state is written to the slot.  Returns o [N,H,192].
+    """
+    N, H, _ = q.shape
+    dev = q.device
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    _need(q, "q", (N, H, DK), q.dtype, dev)
+    _need(k, "k", (N, H, DK), q.dtype, dev)
+    _need(v, "v", (N, H, DV), q.dtype, dev)
+    _need(g, "g", (N, H), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-d tensor of n_seq + 1 offsets")
+    n_seq = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (n_seq + 1,), torch.int32, dev)
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", (n_seq,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((N, H, DV), dtype=_torch_dtype(out_code), device=dev)
+    _need(o, "o", (N, H, DV), _torch_dtype(out_code), dev)
+    dims = _dims(n_seq, int(max_seqlen), H, in_code, out_code)
+    ws = _workspace(gla_workspace_size(GLA_OP_FWD, dims), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gla_chunk_fwd_varlen(ctypes.byref(dims), N, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(g), pool.handle, _ptr(slot_idx), int(bool(init_from_pool)),
+                                      _ptr(o), _ptr(ws), nbytes, _stream()))
+    return o
 
 
 def gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None, want_dS0=False,

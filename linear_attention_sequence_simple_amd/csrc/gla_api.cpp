@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -194,7 +195,8 @@ WalkArgs pass1_args(WalkArgs a, const SegPlan& sp, StateView seg, float* seg_dec
   set_plan(a, sp);
   a.cps = sp.cps / sp.fine;
   a.zinit = StateView{};
-  a.zfin = seg;
+  a.zfin = seg;                                   // rows of the workspace: by sequence, never by slot
+  a.zinit_idx = a.zfin_idx = nullptr;
   a.zfin_only_seg = -1;
   a.seg_decay = seg_decay;
   a.seg_decay_bh_stride = sp.entries();
@@ -204,12 +206,13 @@ WalkArgs pass1_args(WalkArgs a, const SegPlan& sp, StateView seg, float* seg_dec
 }
 
 // Pass 1 and a scan over the parts from z0, which leaves in `seg` the state
-// entering every part.  z0 and seg share one layout.
-hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, const float* z0, StateView seg,
-                          float* seg_decay, int64_t BH, hipStream_t st) {
+// entering every part.  z0 and seg share one layout; z0_idx (or null) maps
+// batch indices to rows of z0.
+hipError_t segment_states(WalkArgs a, int state_variant, const SegPlan& sp, const float* z0, const int32_t* z0_idx,
+                          int H, StateView seg, float* seg_decay, int64_t BH, hipStream_t st) {
   hipError_t e = launch_walk(pass1_args(a, sp, seg, seg_decay), state_variant, pass1_workgroups(sp, BH), st);
   if (e != hipSuccess) return e;
-  return launch_seg_scan(seg.p, seg_decay, z0, BH, sp.entries(), 0, st);
+  return launch_seg_scan(seg.p, seg_decay, z0, z0_idx, H, BH, sp.entries(), 0, st);
 }
 
 // The walk of every segment from its entering state (zinit: the segment
@@ -282,6 +285,47 @@ BwdPlan plan_bwd(const gla_dims* d) {
   p.off_decr = off; off += dec;
   p.ws_total = off;
   return p;
+}
+
+// The forward's walk arguments over [B,T,H,cols] tensors (T of dims), with
+// sequences of at most max_len tokens.
+WalkArgs fwd_args(const gla_dims* dims, const FwdPlan& p, const void* q, const void* k, const void* v,
+                  const float* g, void* o, int64_t max_len) {
+  const size_t isz = dims->in_dtype == GLA_BF16 ? 2 : 4, osz = dims->out_dtype == GLA_BF16 ? 2 : 4;
+  const int w = DV / p.ns;                        // dv-slice width
+  WalkArgs a{};
+  a.X = tok_view(k, isz, dims, DK, 0, false);
+  a.Y = tok_view(v, isz, dims, DV, w, false);
+  a.Q = tok_view(q, isz, dims, DK, 0, false);
+  a.O = tok_view(o, osz, dims, DV, w, false);
+  a.g = g;
+  a.gsb = dims->T * dims->H;
+  a.gsh = 1;
+  a.gst = dims->H;
+  a.B = dims->B;
+  a.T = max_len;
+  a.H = dims->H;
+  return a;
+}
+
+// The forward's launches: one walk per (sequence, head, slice), or pass 1,
+// the segment scan and the walks of all segments.  z0 (p null: zero) and
+// zfin (p null: not written) may be the same memory; a packed walk reaches
+// them through a.zinit_idx and a.zfin_idx.
+hipError_t run_fwd(const gla_dims* dims, const FwdPlan& p, WalkArgs a, StateView z0, StateView zfin, void* ws,
+                   hipStream_t st) {
+  const int64_t BH = dims->B * dims->H;
+  const SegPlan sp{p.ns, p.nseg, p.cps, p.n_chunks, p.fine};
+  if (p.nseg == 1) return walk_segments(a, p.variant, sp, z0, zfin, BH, st);
+  char* wsb = (char*)ws;
+  const StateView seg = seg_view((float*)wsb, z0, sp.entries());
+  const int state_variant = dims->in_dtype == GLA_BF16 ? WV_FWD_STATE_BF16 : WV_FWD_STATE_F32;
+  const int32_t* z0_idx = a.zinit_idx;
+  a.zinit_idx = nullptr;                          // the segment states are indexed by sequence
+  hipError_t e = segment_states(a, state_variant, sp, z0.p, z0_idx, dims->H, seg,
+                                (float*)(wsb + p.ws_seg_states), BH, st);
+  if (e == hipSuccess) e = walk_segments(a, p.variant, sp, coarse(seg, sp), zfin, BH, st);
+  return e;
 }
 
 }  // namespace
@@ -381,35 +425,56 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, con
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
-  const size_t isz = dims->in_dtype == GLA_BF16 ? 2 : 4, osz = dims->out_dtype == GLA_BF16 ? 2 : 4;
-  const int w = DV / p.ns;                        // dv-slice width
-  WalkArgs a{};
-  a.X = tok_view(k, isz, dims, DK, 0, false);
-  a.Y = tok_view(v, isz, dims, DV, w, false);
-  a.Q = tok_view(q, isz, dims, DK, 0, false);
-  a.O = tok_view(o, osz, dims, DV, w, false);
-  a.g = g;
-  a.gsb = dims->T * dims->H;
-  a.gsh = 1;
-  a.gst = dims->H;
-  a.B = dims->B;
-  a.T = dims->T;
-  a.H = dims->H;
-  const int64_t BH = dims->B * dims->H;
-  const SegPlan sp{p.ns, p.nseg, p.cps, p.n_chunks, p.fine};
-  const StateView z0 = state_plain(const_cast<float*>(S0), w), zfin = state_plain(S_T, w);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  if (p.nseg > 1) {
-    char* wsb = (char*)ws;
-    const StateView seg = seg_view((float*)wsb, z0, sp.entries());
-    const int state_variant = dims->in_dtype == GLA_BF16 ? WV_FWD_STATE_BF16 : WV_FWD_STATE_F32;
-    e = segment_states(a, state_variant, sp, S0, seg, (float*)(wsb + p.ws_seg_states), BH, st);
-    if (e == hipSuccess) e = walk_segments(a, p.variant, sp, coarse(seg, sp), zfin, BH, st);
-  } else {
-    e = walk_segments(a, p.variant, sp, z0, zfin, BH, st);
-  }
+  WalkArgs a = fwd_args(dims, p, q, k, v, g, o, dims->T);
+  const int w = DV / p.ns;
+  const hipError_t e = run_fwd(dims, p, a, state_plain(const_cast<float*>(S0), w), state_plain(S_T, w), ws,
+                               (hipStream_t)stream);
   return device_err(e, "gla_chunk_fwd launch");
+}
+
+gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens, const void* q,
+                                const void* k, const void* v, const float* g, gla_state* pool,
+                                const int32_t* slot_idx, int32_t init_from_pool, void* o, void* ws, size_t ws_bytes,
+                                void* stream) {
+  TRY(check_dims(dims));
+  if (total_tokens < 0 || total_tokens > INT32_MAX)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "total_tokens must be in [0, 2^31) (got %lld)", (long long)total_tokens);
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u))
+    return fail(GLA_ERR_INVALID_ARGUMENT, "cu_seqlens must be a non-NULL, 4-byte aligned device array");
+  if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
+  if (!pool) return fail(GLA_ERR_INVALID_ARGUMENT, "pool must not be NULL");
+  if (pool->H != dims->H || pool->dk != dims->dk || pool->dv != dims->dv)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "pool holds H=%d dk=%d dv=%d, call has H=%d dk=%d dv=%d", pool->H,
+                pool->dk, pool->dv, dims->H, dims->dk, dims->dv);
+  if (!slot_idx && dims->B > pool->n_slots)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "B=%lld sequences exceed the pool's %lld slots", (long long)dims->B,
+                (long long)pool->n_slots);
+  if (init_from_pool != 0 && init_from_pool != 1)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_pool must be 0 or 1 (got %d)", init_from_pool);
+  TRY(check_ptr(q, "q", false));
+  TRY(check_ptr(k, "k", false));
+  TRY(check_ptr(v, "v", false));
+  TRY(check_ptr(g, "g", false));
+  TRY(check_ptr(o, "o", false));
+  const FwdPlan p = plan_fwd(dims);
+  if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
+  if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  // packed [total_tokens, H, cols] tensors: one "batch" row holding every token
+  gla_dims packed = *dims;
+  packed.B = 1;
+  packed.T = total_tokens;
+  WalkArgs a = fwd_args(&packed, p, q, k, v, g, o, dims->T);
+  a.X.sb = a.Y.sb = a.Q.sb = a.O.sb = 0;
+  a.gsb = 0;
+  a.B = dims->B;
+  a.cu = cu_seqlens;
+  a.cu_total = total_tokens;
+  a.zinit_idx = a.zfin_idx = slot_idx;
+  const int w = DV / p.ns;
+  const StateView zfin = state_plain(pool->data, w);
+  const StateView z0 = init_from_pool ? zfin : state_plain(nullptr, w);
+  const hipError_t e = run_fwd(dims, p, a, z0, zfin, ws, (hipStream_t)stream);
+  return device_err(e, "gla_chunk_fwd_varlen launch");
 }
 
 gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
@@ -520,8 +585,8 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
     float* dec_r = (float*)(w + p.off_decr);
     const int n1 = pass1_workgroups(sp, BH);
     e = launch_state_walk_pair(pass1_args(f, sp, fseg, dec_f), n1, pass1_args(r, sp, rseg, dec_r), n1, st);
-    if (e == hipSuccess) e = launch_seg_scan(fseg.p, dec_f, S0, BH, sp.entries(), 0, st);
-    if (e == hipSuccess) e = launch_seg_scan(rseg.p, dec_r, dS_T, BH, sp.entries(), 0, st);
+    if (e == hipSuccess) e = launch_seg_scan(fseg.p, dec_f, S0, nullptr, dims->H, BH, sp.entries(), 0, st);
+    if (e == hipSuccess) e = launch_seg_scan(rseg.p, dec_r, dS_T, nullptr, dims->H, BH, sp.entries(), 0, st);
     if (e != hipSuccess) return device_err(e, "gla_chunk_bwd segment states");
     fseg = coarse(fseg, sp);
     rseg = coarse(rseg, sp);

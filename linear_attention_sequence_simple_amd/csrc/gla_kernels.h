@@ -58,6 +58,16 @@ struct WalkArgs {
   int64_t seg_decay_bh_stride;
   int64_t B, T;
   int H, n_chunks, cps, ns, nseg_launch, seg_offset;
+  // Packed sequences (null: B sequences of T tokens): sequence b is tokens
+  // [cu[b], cu[b+1]) of a token axis of cu_total rows, the batch strides are
+  // zero, and T and n_chunks bound its length in tokens and chunks.  Offsets
+  // are clamped into [0, cu_total] and lengths to [0, T].
+  const int32_t* cu;
+  int64_t cu_total;
+  // Packed sequences only: the batch index of sequence b's initial (final)
+  // state is zinit_idx[b] (zfin_idx[b]), a slot of a pool; null: b.
+  const int32_t* zinit_idx;
+  const int32_t* zfin_idx;
 };
 
 hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st);
@@ -68,8 +78,9 @@ hipError_t launch_out_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1
                                 hipStream_t st);
 hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st);
 int walk_slices(int variant);
-hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, int64_t BH, int nseg, int rev,
-                           hipStream_t st);
+// Z0 row of batch-head bh: z0_idx[bh / H] * H + bh % H when z0_idx is set.
+hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, const int32_t* z0_idx, int H,
+                           int64_t BH, int nseg, int rev, hipStream_t st);
 
 // Decode step: see gla_step.hip.
 struct StepArgs {

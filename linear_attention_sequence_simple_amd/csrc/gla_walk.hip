@@ -179,7 +179,32 @@ struct TileRegs {
   }
 };
 
-template <class TIn, class TOut, int NC, int MODE, int W>
+// The tokens of walk b: first token, length and chunk count.  PACKED walks
+// take them from the sequence offsets, the others from the launch.
+struct SeqSpan {
+  int64_t t0, T;
+  int n_chunks;
+};
+template <bool PACKED>
+__device__ __forceinline__ SeqSpan seq_span(const WalkArgs& a, int b) {
+  if constexpr (!PACKED) {
+    return SeqSpan{0, a.T, a.n_chunks};
+  } else {
+    const int64_t t0 = min(max((int64_t)a.cu[b], (int64_t)0), a.cu_total);
+    const int64_t end = min(max((int64_t)a.cu[b + 1], t0), min(a.cu_total, t0 + a.T));
+    const int64_t T = end - t0;
+    return SeqSpan{t0, T, (int)((T + CH - 1) / CH)};
+  }
+}
+// Row of batch-head (b, h) in a state view, through the slot indices idx of
+// packed walks.
+template <bool PACKED>
+__device__ __forceinline__ int64_t state_row(const int32_t* idx, int b, int h, int H) {
+  if constexpr (PACKED) return (int64_t)(idx ? idx[b] : b) * H + h;
+  return (int64_t)b * H + h;
+}
+
+template <class TIn, class TOut, int NC, int MODE, int W, bool PACKED>
 __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm,
                                           int b, int h, int slice, int seg) {
   constexpr bool OUT = MODE == WALK_FWD_OUT;
@@ -199,22 +224,23 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   const int lane = lane_id();
   const int g2 = lane >> 5;
   const int64_t bh = (int64_t)b * a.H + h;
-  const int64_t T = a.T;
-  const TIn* Xb = (const TIn*)a.X.p + b * a.X.sb + h * a.X.sh + slice * a.X.ss;
-  const TIn* Yb = (const TIn*)a.Y.p + b * a.Y.sb + h * a.Y.sh + slice * a.Y.ss;
-  const TIn* Qb = OUT ? (const TIn*)a.Q.p + b * a.Q.sb + h * a.Q.sh + slice * a.Q.ss : nullptr;
-  const float* gb = a.g + b * a.gsb + h * a.gsh;
+  const SeqSpan sq = seq_span<PACKED>(a, b);
+  const int64_t T = sq.T;
+  const TIn* Xb = (const TIn*)a.X.p + b * a.X.sb + sq.t0 * a.X.st + h * a.X.sh + slice * a.X.ss;
+  const TIn* Yb = (const TIn*)a.Y.p + b * a.Y.sb + sq.t0 * a.Y.st + h * a.Y.sh + slice * a.Y.ss;
+  const TIn* Qb = OUT ? (const TIn*)a.Q.p + b * a.Q.sb + sq.t0 * a.Q.st + h * a.Q.sh + slice * a.Q.ss : nullptr;
+  const float* gb = a.g + b * a.gsb + sq.t0 * a.gst + h * a.gsh;
 
   const int gseg = seg + a.seg_offset;
   const int n_begin = gseg * a.cps;
-  const int n_end = min(a.n_chunks, n_begin + a.cps);
-  const int nloc = n_end - n_begin;
+  const int n_end = min(sq.n_chunks, n_begin + a.cps);
+  const int nloc = PACKED ? max(0, n_end - n_begin) : n_end - n_begin;   // packed: past a sequence's end, 0
 
   // ---- state tiles Z^T (c rows, d columns): initial state or zero
   f32x16 z[NT > 0 ? NT : 1];
   {
     const StateView& zv = a.zinit;
-    const float* zi = zv.p ? zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss : nullptr;
+    const float* zi = zv.p ? zv.p + state_row<PACKED>(a.zinit_idx, b, h, a.H) * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss : nullptr;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
@@ -377,7 +403,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
             o[cb] = mfma(frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s), pf[J][s], o[cb]);
       const int64_t trow = (int64_t)n * CH + il;
       if (trow < T) {
-        TOut* op = (TOut*)a.O.p + b * a.O.sb + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
+        TOut* op = (TOut*)a.O.p + b * a.O.sb + sq.t0 * a.O.st + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
@@ -464,7 +490,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   // ---- final state
   if (a.zfin.p && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
     const StateView& zv = a.zfin;
-    float* zo = zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss;
+    float* zo = zv.p + state_row<PACKED>(a.zfin_idx, b, h, a.H) * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
@@ -504,7 +530,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 // overlaps the products.  All tiles are read from memory with row-contiguous
 // 16-byte accesses, spread over both phases so that the workgroups on the
 // chip keep the memory busy instead of all loading at the same moment.
-template <class TOut, int W>
+template <class TOut, int W, bool PACKED>
 __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3, true>& sm, int b, int h,
                                              int slice, int seg) {
   using S = WalkSmem<bf16, 3, true>;
@@ -519,21 +545,22 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   const int lane = lane_id();
   const int g2 = lane >> 5;
   const int64_t bh = (int64_t)b * a.H + h;
-  const int64_t T = a.T;
-  const bf16* Xb = (const bf16*)a.X.p + b * a.X.sb + h * a.X.sh + slice * a.X.ss;
-  const bf16* Yb = (const bf16*)a.Y.p + b * a.Y.sb + h * a.Y.sh + slice * a.Y.ss;
-  const bf16* Qb = (const bf16*)a.Q.p + b * a.Q.sb + h * a.Q.sh + slice * a.Q.ss;
-  const float* gb = a.g + b * a.gsb + h * a.gsh;
+  const SeqSpan sq = seq_span<PACKED>(a, b);
+  const int64_t T = sq.T;
+  const bf16* Xb = (const bf16*)a.X.p + b * a.X.sb + sq.t0 * a.X.st + h * a.X.sh + slice * a.X.ss;
+  const bf16* Yb = (const bf16*)a.Y.p + b * a.Y.sb + sq.t0 * a.Y.st + h * a.Y.sh + slice * a.Y.ss;
+  const bf16* Qb = (const bf16*)a.Q.p + b * a.Q.sb + sq.t0 * a.Q.st + h * a.Q.sh + slice * a.Q.ss;
+  const float* gb = a.g + b * a.gsb + sq.t0 * a.gst + h * a.gsh;
   const int gseg = seg + a.seg_offset;
   const int n_begin = gseg * a.cps;
-  const int n_end = min(a.n_chunks, n_begin + a.cps);
-  const int nloc = n_end - n_begin;
+  const int n_end = min(sq.n_chunks, n_begin + a.cps);
+  const int nloc = PACKED ? max(0, n_end - n_begin) : n_end - n_begin;   // packed: past a sequence's end, 0
 
   // ---- state tiles Z^T (c rows, d columns): initial state or zero
   f32x16 z[NT > 0 ? NT : 1];
   {
     const StateView& zv = a.zinit;
-    const float* zi = zv.p ? zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss : nullptr;
+    const float* zi = zv.p ? zv.p + state_row<PACKED>(a.zinit_idx, b, h, a.H) * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss : nullptr;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
@@ -759,7 +786,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
         // the dot product of each output row with a row of D.
         const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
         const bool live = trow < T;
-        const float* ap = (const float*)a.acc.p + b * a.acc.sb + h * a.acc.sh + trow * a.acc.st + 4 * g2;
+        const float* ap = (const float*)a.acc.p + b * a.acc.sb + sq.t0 * a.acc.st + h * a.acc.sh + trow * a.acc.st + 4 * g2;
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
@@ -769,7 +796,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
             for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] += v[e];
           }
         if (a.rdot.p) {
-          const bf16* dp = (const bf16*)a.D.p + b * a.D.sb + h * a.D.sh + trow * a.D.st + 4 * g2;
+          const bf16* dp = (const bf16*)a.D.p + b * a.D.sb + sq.t0 * a.D.st + h * a.D.sh + trow * a.D.st + 4 * g2;
           float r = 0.f;
 #pragma unroll
           for (int cb = 0; cb < NC; ++cb)
@@ -781,7 +808,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
             }
           r += __shfl_xor(r, 32, 64);
           if (g2 == 0 && live)
-            ((float*)a.rdot.p)[b * a.rdot.sb + h * a.rdot.sh + trow * a.rdot.st] = r;
+            ((float*)a.rdot.p)[b * a.rdot.sb + (sq.t0 + trow) * a.rdot.st + h * a.rdot.sh] = r;
         }
       }
       if constexpr (std::is_same<TOut, bf16>::value) {
@@ -790,7 +817,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
         // in the accumulator layout, read back and stored as row-contiguous
         // 16-byte pieces.
         bf16* ot = sm.q + 32 * W * 96;
-        const bf16* ob = (const bf16*)a.O.p + b * a.O.sb + h * a.O.sh + slice * a.O.ss;
+        const bf16* ob = (const bf16*)a.O.p + b * a.O.sb + sq.t0 * a.O.st + h * a.O.sh + slice * a.O.ss;
         const int64_t t0 = (int64_t)n * CH + 32 * W;
         char* tile = const_cast<char*>(tile_base(ob, a.O.st, t0, 32));
 #pragma unroll
@@ -808,7 +835,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
       } else {
         const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
         if (trow < T) {
-          TOut* op = (TOut*)a.O.p + b * a.O.sb + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
+          TOut* op = (TOut*)a.O.p + b * a.O.sb + sq.t0 * a.O.st + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
 #pragma unroll
           for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
@@ -862,7 +889,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   // ---- final state
   if (a.zfin.p && (a.zfin_only_seg < 0 || a.zfin_only_seg == gseg)) {
     const StateView& zv = a.zfin;
-    float* zo = zv.p + bh * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss;
+    float* zo = zv.p + state_row<PACKED>(a.zfin_idx, b, h, a.H) * zv.sbh + (int64_t)gseg * zv.sseg + slice * zv.ss;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
@@ -883,7 +910,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
 }
 
 // The walk of workgroup `local` of a launch of `nwg` workgroups.
-template <class TIn, class TOut, int NC, int MODE>
+template <class TIn, class TOut, int NC, int MODE, bool PACKED = false>
 __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm, int local,
                                            int nwg) {
   // Work item order: slice fastest, then segment, head, batch.  Consecutive
@@ -900,29 +927,29 @@ __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, 
   const int b = rest / a.H;
   if constexpr (MODE == WALK_FWD_OUT && std::is_same<TIn, bf16>::value) {
     switch (threadIdx.x >> 6) {
-      case 0: prefill_wave<TOut, 0>(a, sm, b, h, slice, seg); break;
-      case 1: prefill_wave<TOut, 1>(a, sm, b, h, slice, seg); break;
-      case 2: prefill_wave<TOut, 2>(a, sm, b, h, slice, seg); break;
-      case 3: prefill_wave<TOut, 3>(a, sm, b, h, slice, seg); break;
-      case 4: prefill_wave<TOut, 4>(a, sm, b, h, slice, seg); break;
-      case 5: prefill_wave<TOut, 5>(a, sm, b, h, slice, seg); break;
-      case 6: prefill_wave<TOut, 6>(a, sm, b, h, slice, seg); break;
-      default: prefill_wave<TOut, 7>(a, sm, b, h, slice, seg); break;
+      case 0: prefill_wave<TOut, 0, PACKED>(a, sm, b, h, slice, seg); break;
+      case 1: prefill_wave<TOut, 1, PACKED>(a, sm, b, h, slice, seg); break;
+      case 2: prefill_wave<TOut, 2, PACKED>(a, sm, b, h, slice, seg); break;
+      case 3: prefill_wave<TOut, 3, PACKED>(a, sm, b, h, slice, seg); break;
+      case 4: prefill_wave<TOut, 4, PACKED>(a, sm, b, h, slice, seg); break;
+      case 5: prefill_wave<TOut, 5, PACKED>(a, sm, b, h, slice, seg); break;
+      case 6: prefill_wave<TOut, 6, PACKED>(a, sm, b, h, slice, seg); break;
+      default: prefill_wave<TOut, 7, PACKED>(a, sm, b, h, slice, seg); break;
     }
     return;
   } else {
   switch (threadIdx.x >> 6) {
-    case 0: walk_wave<TIn, TOut, NC, MODE, 0>(a, sm, b, h, slice, seg); break;
-    case 1: walk_wave<TIn, TOut, NC, MODE, 1>(a, sm, b, h, slice, seg); break;
-    case 2: walk_wave<TIn, TOut, NC, MODE, 2>(a, sm, b, h, slice, seg); break;
-    case 3: walk_wave<TIn, TOut, NC, MODE, 3>(a, sm, b, h, slice, seg); break;
+    case 0: walk_wave<TIn, TOut, NC, MODE, 0, PACKED>(a, sm, b, h, slice, seg); break;
+    case 1: walk_wave<TIn, TOut, NC, MODE, 1, PACKED>(a, sm, b, h, slice, seg); break;
+    case 2: walk_wave<TIn, TOut, NC, MODE, 2, PACKED>(a, sm, b, h, slice, seg); break;
+    case 3: walk_wave<TIn, TOut, NC, MODE, 3, PACKED>(a, sm, b, h, slice, seg); break;
     default:
       if constexpr (WalkShape<MODE>::WAVES == 8) {
         switch (threadIdx.x >> 6) {
-          case 4: walk_wave<TIn, TOut, NC, MODE, 4>(a, sm, b, h, slice, seg); break;
-          case 5: walk_wave<TIn, TOut, NC, MODE, 5>(a, sm, b, h, slice, seg); break;
-          case 6: walk_wave<TIn, TOut, NC, MODE, 6>(a, sm, b, h, slice, seg); break;
-          default: walk_wave<TIn, TOut, NC, MODE, 7>(a, sm, b, h, slice, seg); break;
+          case 4: walk_wave<TIn, TOut, NC, MODE, 4, PACKED>(a, sm, b, h, slice, seg); break;
+          case 5: walk_wave<TIn, TOut, NC, MODE, 5, PACKED>(a, sm, b, h, slice, seg); break;
+          case 6: walk_wave<TIn, TOut, NC, MODE, 6, PACKED>(a, sm, b, h, slice, seg); break;
+          default: walk_wave<TIn, TOut, NC, MODE, 7, PACKED>(a, sm, b, h, slice, seg); break;
         }
       }
       break;
@@ -936,10 +963,10 @@ __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, 
 template <class TIn, int MODE>
 constexpr int walk_waves_per_eu() { return (MODE == WALK_FWD_STATE && sizeof(TIn) == 2) ? 2 : 1; }
 
-template <class TIn, class TOut, int NC, int MODE>
+template <class TIn, class TOut, int NC, int MODE, bool PACKED>
 __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, (walk_waves_per_eu<TIn, MODE>())) walk_kernel(WalkArgs a) {
   __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
-  walk_block<TIn, TOut, NC, MODE>(a, sm, (int)blockIdx.x, (int)gridDim.x);
+  walk_block<TIn, TOut, NC, MODE, PACKED>(a, sm, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Two independent state walks of one kind side by side: workgroups [0, nwg0)
@@ -960,11 +987,12 @@ __global__ void __launch_bounds__(WalkShape<WALK_FWD_STATE>::THREADS, (walk_wave
 // the segment's total log2-decay.  Forward order starts from Z0, reverse order
 // (rev != 0) from the last segment.
 __global__ void __launch_bounds__(256) seg_scan_kernel(float* buf, const float* decay, const float* Z0,
-                                                       int nseg, int rev) {
+                                                       const int32_t* z0_idx, int H, int nseg, int rev) {
   const int64_t bh = blockIdx.y;
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= DK * DV) return;
-  f32x4 z = Z0 ? *(const f32x4*)(Z0 + bh * DK * DV + e) : f32x4{0, 0, 0, 0};
+  const int64_t zrow = z0_idx ? (int64_t)z0_idx[bh / H] * H + bh % H : bh;
+  f32x4 z = Z0 ? *(const f32x4*)(Z0 + zrow * DK * DV + e) : f32x4{0, 0, 0, 0};
   for (int it = 0; it < nseg; ++it) {
     const int s = rev ? nseg - 1 - it : it;
     float* p = buf + (bh * nseg + s) * (int64_t)(DK * DV) + e;
@@ -977,7 +1005,10 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(float* buf, const float* 
 // ---------------------------------------------------------------------------
 template <class TIn, class TOut, int NC, int MODE>
 static hipError_t launch_one(const WalkArgs& a, int nwg, hipStream_t st) {
-  hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE>), dim3(nwg), dim3(WalkShape<MODE>::THREADS), 0, st, a);
+  if (a.cu)
+    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, true>), dim3(nwg), dim3(WalkShape<MODE>::THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, false>), dim3(nwg), dim3(WalkShape<MODE>::THREADS), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1024,10 +1055,10 @@ int walk_slices(int variant) {
   }
 }
 
-hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, int64_t BH, int nseg, int rev,
-                           hipStream_t st) {
+hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, const int32_t* z0_idx, int H,
+                           int64_t BH, int nseg, int rev, hipStream_t st) {
   hipLaunchKernelGGL(seg_scan_kernel, dim3((DK * DV / 4 + 255) / 256, (unsigned)BH), dim3(256), 0, st, buf,
-                     decay, Z0, nseg, rev);
+                     decay, Z0, z0_idx, H, nseg, rev);
   return hipGetLastError();
 }
 

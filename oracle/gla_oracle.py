@@ -27,13 +27,14 @@ Everything is float64.  Inputs may be any float dtype; callers pass the exact
 values the device sees (bf16 inputs already rounded to bf16).
 
 Layouts: q, k [B, T, H, dk]; v, o, dO [B, T, H, dv]; g [B, T, H];
-S0, S_T, dS_T, dS0 [B, H, dk, dv].
+S0, S_T, dS_T, dS0 [B, H, dk, dv]; packed sequences: [N, H, ...] rows split
+by sequence offsets, states in a pool [n_slots, H, dk, dv].
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "step", "backward", "state_bytes"]
+__all__ = ["forward", "forward_packed", "step", "backward", "state_bytes"]
 
 
 def _f64(x):
@@ -130,6 +131,41 @@ def backward(q, k, v, g, dO, S0=None, dS_T=None, ckpt=16):
             dg[:, t] = gam[:, t] * np.einsum("bhij,bhij->bh", U, S_prev)
             U *= gam[:, t, :, None, None]
     return dq, dkk, dvv, dg, U
+
+
+def forward_packed(q, k, v, g, cu_seqlens, pool, slot_idx=None, init_from_pool=False):
+    """Prefill of sequences of different lengths packed along one token axis,
+    each with its state in a slot of a pool.
+
+    The pages serve many concurrent sequences with each one's recurrent state
+    held in a memory pool, and prompts of different lengths ("AWS serve
+    Laplace 3B di i14 con uno stato fisso di 29,5 MB", sections "Lo stato di
+    Laplace 3B resta fisso durante l'inferenza" and "I risultati dichiarati
+    hanno limiti precisi").  Sequence b is rows cu_seqlens[b] to
+    cu_seqlens[b+1] of q, k [N, H, dk], v [N, H, dv], g [N, H]; it runs the
+    recurrence of `forward` on its own, from its slot's state when
+    init_from_pool is set (else from zero), and its final state replaces
+    that slot.  slot_idx[b] is sequence b's slot (None: slot b).
+
+    Returns (o [N, H, dv], new pool [n_slots, H, dk, dv]) in float64; the
+    pool passed in is not modified and slots of no sequence keep their state.
+    """
+    q, k, v, g, pool = _f64(q), _f64(k), _f64(v), _f64(g), _f64(pool)
+    cu = [int(c) for c in cu_seqlens]
+    n_seq = len(cu) - 1
+    slots = list(range(n_seq)) if slot_idx is None else [int(s) for s in slot_idx]
+    o = np.zeros((q.shape[0], q.shape[1], v.shape[-1]))
+    new_pool = pool.copy()
+    for b in range(n_seq):
+        t0, t1 = cu[b], cu[b + 1]
+        S0 = pool[slots[b]][None] if init_from_pool else None
+        if t1 == t0:
+            new_pool[slots[b]] = pool[slots[b]] if init_from_pool else 0.0
+            continue
+        ob, S = forward(q[None, t0:t1], k[None, t0:t1], v[None, t0:t1], g[None, t0:t1], S0)
+        o[t0:t1] = ob[0]
+        new_pool[slots[b]] = S[0]
+    return o, new_pool
 
 
 def state_bytes(H, dk, dv, itemsize=4):

@@ -99,3 +99,18 @@ def test_state_pool_validation(L):
     assert L.gla_state_slots(None) == 0
     assert L.gla_state_slot_bytes(16, 96, 192) == 1_179_648
     assert L.gla_state_free(None) == 0
+
+
+def test_packed_prefill_validation(L):
+    d = dims()
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    call = lambda total, cu, pool, init=0, slots=None: L.gla_chunk_fwd_varlen(
+        ctypes.byref(d), total, cu, p, p, p, p, pool, slots, init, p, None, 0, None)
+    assert call(-1, p, p) == 1 and "total_tokens" in L.gla_last_error().decode()
+    assert call(1 << 31, p, p) == 1
+    assert call(10, None, p) == 1 and "cu_seqlens" in L.gla_last_error().decode()
+    assert call(10, ctypes.c_void_p(0x10002), p) == 1 and "cu_seqlens" in L.gla_last_error().decode()
+    assert call(10, p, p, slots=ctypes.c_void_p(0x10001)) == 1 and "slot_idx" in L.gla_last_error().decode()
+    assert call(10, p, None) == 1 and "pool" in L.gla_last_error().decode()
+    bad = gla.GlaDims(B=2, T=0, H=16, dk=96, dv=192, chunk=128, in_dtype=1, out_dtype=1)
+    assert L.gla_chunk_fwd_varlen(ctypes.byref(bad), 10, p, p, p, p, p, p, None, 0, p, None, 0, None) == 1
