@@ -11,14 +11,16 @@ resident in HBM.  The same line carries, measured in the same run:
             fp32 state read and written in place (GB/s of state traffic)
   backward  chunked backward, B=4, H=16, T=4096 (tokens/s)
   long_context  prefill B=1, T=65536 with a non-zero initial state
+  packed    serving prefill: 16 prompts of 2,048-8,192 tokens packed along
+            one token axis, final states written into a 1,280-slot pool
   fp32      prefill B=1, T=2048 with fp32 inputs and outputs
   roofline  the prefill walk kernel against the HBM roof (HIP events)
   cpu_baseline  the fp64 oracle on the host cores, whole workload
   parity    sampled max|err|/rms(ref) against the oracle for this run
 
 --only PART runs a single part a few times (for profiler counter passes):
-prefill | decode | backward | copy (a plain 1 GiB device copy used to scale
-the HBM byte counters).
+prefill | decode | backward | packed | copy (a plain 1 GiB device copy used
+to scale the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -55,6 +57,13 @@ def fwd_bytes(B, T, in_b, out_b, s0=False):
     th = B * T * H
     per = (2 * DK + DV) * in_b + 4 + DV * out_b
     return th * per + B * H * DK * DV * 4 * (2 if s0 else 1)
+
+
+def packed_bytes(n_tokens, n_seq, in_b, out_b, init=False):
+    """Packed prefill: every token's q, k, v, g read and o written once; each
+    sequence's final state written to its slot (and its initial one read)."""
+    per = (2 * DK + DV) * in_b + 4 + DV * out_b
+    return n_tokens * H * per + n_seq * H * DK * DV * 4 * (2 if init else 1)
 
 
 def bwd_bytes(B, T, in_b, out_b):
@@ -219,6 +228,34 @@ def bench_prefill_other(torch, gla, name, in_dtype, out_dtype, steps, warmup):
             "mfma_peak": f"{'bf16' if ib == 2 else 'fp32'} {peak} TFLOP/s"}
 
 
+def bench_packed(torch, gla, steps, warmup):
+    d = gen.make_packed_inputs("serve_prefill_16x2k8k", seed=0, with_pool=False)
+    w = d["meta"]
+    dev = torch.device("cuda", 0)
+    T = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    q, k, v = (T(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    g = T(d["g"], torch.float32)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+    slots = torch.from_numpy(d["slot_idx"]).to(dev)
+    N, n_seq = int(d["cu_seqlens"][-1]), len(d["slot_idx"])
+    pool = gla.gla_state_alloc(w["n_slots"])
+    o = torch.empty((N, H, DV), dtype=torch.bfloat16, device=dev)
+    dims = gla.GlaDims(n_seq, w["len_hi"], H, DK, DV, CH, gla.GLA_BF16, gla.GLA_BF16)
+    ws = torch.empty(max(gla.gla_workspace_size(gla.GLA_OP_FWD, dims), 1), dtype=torch.uint8, device=dev)
+    fn = lambda: gla.gla_chunk_fwd_varlen(q, k, v, g, cu, w["len_hi"], pool, slots, init_from_pool=False,
+                                          out_dtype=torch.bfloat16, workspace=ws, o=o)
+    ms, _ = _time_calls(torch, fn, steps, warmup)
+    pool.free()
+    nbytes = packed_bytes(N, n_seq, 2, 2)
+    flops = FWD_FLOP_PER_TH * N * H
+    lens = w["lengths"]
+    return {"workload": f"packed prefill, {n_seq} prompts of {int(lens.min())}-{int(lens.max())} tokens "
+                        f"({N} in all), H=16 bf16 in/out, final states into a {w['n_slots']}-slot pool",
+            "ms": ms, "tokens_per_s": N / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "bytes": nbytes}
+
+
 def bench_decode(torch, gla, layers=24, steps=64, warmup=1, parity=True):
     w = gen.WORKLOADS["decode_1280x24x64"]
     n = w["B"]
@@ -330,7 +367,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "copy"], default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -347,6 +384,8 @@ def main():
                                           parity=False)))
         elif args.only == "backward":
             print(json.dumps(bench_backward(torch, gla, args.steps, args.warmup)))
+        elif args.only == "packed":
+            print(json.dumps(bench_packed(torch, gla, args.steps, args.warmup)))
         else:
             n = 1 << 28
             a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -372,6 +411,8 @@ def main():
                              max(3, args.steps // 2), 2)
     f32 = bench_prefill_other(torch, gla, "fwd_f32_b1_t2048", torch.float32, torch.float32,
                               max(3, args.steps // 2), 2)
+    packed = bench_packed(torch, gla, max(3, args.steps // 2), 2)
+    print(f"[bench] packed {packed['ms']:.4f} ms", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms"], "higher_is_better": True,
@@ -381,12 +422,12 @@ def main():
                    "global_batch": 8, "seq_len": 2048, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": pre["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pre["GBps"] / HBM_PEAK_GBS, "traffic": traffic_from_profiles(),
-                     "kernel": "walk_kernel<bf16,bf16,3,0> (gla_chunk_fwd)",
+                     "kernel": "walk_kernel<bf16,bf16,3,0,false> (gla_chunk_fwd)",
                      "algorithmic_bytes_per_launch": pre["bytes"]},
         "mfma_util": {"value": pre["mfma_util"], "algorithmic_flop_per_step": pre["flops"],
                       "peak": "bf16 dense 2500 TFLOP/s",
                       "note": "dense 128-token chunks; the HBM roof caps this at ~0.40 for this workload"},
-        "decode": dec, "backward": bwd, "long_context": lc, "fp32": f32,
+        "decode": dec, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed,
         "parity": {"prefill": pre.get("parity")},
         "cpu_baseline": cpu,
         "kernel_source_digest": src_digest(),

@@ -909,22 +909,52 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
     a.seg_decay[bh * a.seg_decay_bh_stride + gseg] = decay_sum;
 }
 
+// Packed launches of at most 64 sequences walk the longest sequences first:
+// the dispatcher starts workgroups in launch order, so a long sequence left
+// to the end of the launch would still run after the rest of the chip has
+// gone idle.  Returns the sequence of rank i in decreasing length (ties in
+// index order), computed by every wave from the offsets: lane c holds
+// sequence c's length and counts the sequences that precede it.
+__device__ __forceinline__ int longest_first(const WalkArgs& a, int i) {
+  if (a.B > 64) return i;
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < a.B;
+  const long long len = live ? (long long)a.cu[lane + 1] - a.cu[lane] : -1;
+  int rank = 0;
+  for (int j = 0; j < 64; ++j) {
+    const long long lj = __shfl(len, j, 64);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const unsigned long long pick = __ballot(live && rank == i);
+  return __ffsll(pick) - 1;
+}
+
 // The walk of workgroup `local` of a launch of `nwg` workgroups.
 template <class TIn, class TOut, int NC, int MODE, bool PACKED = false>
 __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm, int local,
                                            int nwg) {
-  // Work item order: slice fastest, then segment, head, batch.  Consecutive
-  // items are placed on the same XCD (the dispatcher deals workgroups to the
-  // 8 XCDs round-robin), so the dv-slices of one head and neighbouring heads
-  // share that XCD's L2.
+  // Work item order: slice fastest, then segment, head, batch.  Equal-length
+  // walks place consecutive items on the same XCD (the dispatcher deals
+  // workgroups to the 8 XCDs round-robin), so the dv-slices of one head and
+  // neighbouring heads share that XCD's L2.
   int wid = local;
-  if ((nwg & 7) == 0) wid = (local & 7) * (nwg >> 3) + (local >> 3);
+  if constexpr (PACKED) {
+    // Sequences of different lengths: the dv-slices of one head stay on one
+    // XCD (workgroups l and l+8 share one) and consecutive heads go to
+    // consecutive XCDs, so every XCD gets an even share of every sequence
+    // and starts its work in launch order (longest sequences first).
+    const int y = local >> 3;
+    if (nwg % (8 * a.ns) == 0) wid = ((y / a.ns) * 8 + (local & 7)) * a.ns + y % a.ns;
+  } else if ((nwg & 7) == 0) {
+    wid = (local & 7) * (nwg >> 3) + (local >> 3);
+  }
   const int slice = wid % a.ns;
   int rest = wid / a.ns;
   const int seg = rest % a.nseg_launch;
   rest /= a.nseg_launch;
   const int h = rest % a.H;
-  const int b = rest / a.H;
+  int b = rest / a.H;
+  if constexpr (PACKED) b = longest_first(a, b);
   if constexpr (MODE == WALK_FWD_OUT && std::is_same<TIn, bf16>::value) {
     switch (threadIdx.x >> 6) {
       case 0: prefill_wave<TOut, 0, PACKED>(a, sm, b, h, slice, seg); break;
