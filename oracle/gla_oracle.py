@@ -34,7 +34,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "forward_packed", "step", "backward", "state_bytes"]
+__all__ = ["forward", "forward_packed", "step", "backward", "conv1d_silu", "state_bytes"]
 
 
 def _f64(x):
@@ -166,6 +166,49 @@ def forward_packed(q, k, v, g, cu_seqlens, pool, slot_idx=None, init_from_pool=F
         o[t0:t1] = ob[0]
         new_pool[slots[b]] = S[0]
     return o, new_pool
+
+
+def conv1d_silu(x, w, bias, cu_seqlens, state=None, slot_idx=None, init_from_state=False):
+    """Causal depth-wise convolution of width 4 followed by SiLU, per sequence.
+
+    The pages put it ahead of the mixer: every residual vector goes through a
+    causal depth-wise Conv1d of width 4 with SiLU, a 4-gram summary of the
+    recent tokens ("Cómo i14 llevó Laplace 3B a AWS Trainium2", section
+    "Diseño esencial de Laplace 3B").  For channel c of sequence token t,
+
+        a_t[c] = bias[c] + sum_{j=0..3} w[c, j] * x_{t-3+j}[c]
+        y_t[c] = a_t[c] / (1 + exp(-a_t[c]))           (SiLU)
+
+    so w[c, 3] weights the current token.  Tokens before the sequence's first
+    come from its slot of `state` ([n_slots, 3, D], row m holding x_{m-3})
+    when init_from_state is set, else are zero.  x is [N, D] with sequence b
+    at rows cu_seqlens[b] to cu_seqlens[b+1]; w is [D, 4]; bias [D] or None.
+
+    Returns (y [N, D], new state or None) in float64: with a state, each
+    sequence's slot receives the last three inputs of its history followed by
+    its tokens; other slots keep theirs; the state passed in is not modified.
+    """
+    x, w = _f64(x), _f64(w)
+    N, D = x.shape
+    bias = np.zeros(D) if bias is None else _f64(bias)
+    cu = [int(c) for c in cu_seqlens]
+    n_seq = len(cu) - 1
+    slots = list(range(n_seq)) if slot_idx is None else [int(s) for s in slot_idx]
+    state = _f64(state)
+    y = np.zeros((N, D))
+    new_state = None if state is None else state.copy()
+    for b in range(n_seq):
+        t0, t1 = cu[b], cu[b + 1]
+        hist = state[slots[b]] if (state is not None and init_from_state) else np.zeros((3, D))
+        z = np.concatenate([hist, x[t0:t1]], 0)        # z[m] = x_{m-3}
+        for t in range(t1 - t0):
+            a = bias.copy()
+            for j in range(4):
+                a += w[:, j] * z[t + j]
+            y[t0 + t] = a / (1.0 + np.exp(-a))
+        if new_state is not None:
+            new_state[slots[b]] = z[-3:]
+    return y, new_state
 
 
 def state_bytes(H, dk, dv, itemsize=4):
