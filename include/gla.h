@@ -210,6 +210,41 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k,
                          size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Causal depth-wise convolution of width 4 followed by SiLU: the step that
+ * gives every residual vector a summary of its last four tokens before the
+ * fused projection that produces q, k, v and the gate ("Cómo i14 llevó
+ * Laplace 3B a AWS Trainium2", section "Diseño esencial de Laplace 3B").  For
+ * channel c of token t of a sequence:
+ *     a_t[c] = bias[c] + sum_{j=0..3} w[c][j] * x_{t-3+j}[c]
+ *     y_t[c] = a_t[c] / (1 + exp(-a_t[c]))
+ * so w[c][3] weights the current token.  Tokens before a sequence's first
+ * come from its history in conv_state (init_from_state = 1) or are zero.
+ *
+ *   B, T, D : B sequences of at most T tokens, D channels (a multiple of 8;
+ *             3,072 in the pages' model)
+ *   cu_seqlens : NULL: x and y are [B, T, D], every sequence T tokens long.
+ *             Else device int32 [B + 1]: x and y are [total_tokens, D] and
+ *             sequence b is rows [cu_seqlens[b], cu_seqlens[b+1]), with the
+ *             clamping and caller contract of gla_chunk_fwd_varlen.
+ *   x    : in_dtype            y : out_dtype (same layout as x)
+ *   w    : [D, 4] float32      bias : [D] float32 or NULL (zero)
+ *   conv_state : [n_slots, 3, D] in_dtype or NULL; row m of a slot holds
+ *             the input three-minus-m tokens back.  When given, each
+ *             sequence's slot (slot_idx[b], device int32 [B], or b when NULL;
+ *             in range and distinct, a caller contract) receives the last
+ *             three inputs of its history followed by its tokens.  One
+ *             decode step is T = 1.
+ * Errors: INVALID_ARGUMENT (NULL or misaligned pointers, B or T < 1,
+ * init_from_state without conv_state), UNSUPPORTED (D), DEVICE.
+ */
+gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype,
+                           int32_t out_dtype, const int32_t* cu_seqlens,
+                           int64_t total_tokens, const void* x, const float* w,
+                           const float* bias, void* conv_state,
+                           const int32_t* slot_idx, int32_t init_from_state,
+                           void* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Errors. */
 const char* gla_status_str(gla_status status);
 /* Message of the last failing call on this thread ("" if none). */

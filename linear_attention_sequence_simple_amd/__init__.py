@@ -11,6 +11,9 @@ functions carry the names of the C entry points (include/gla.h):
     gla_recurrent_step(pool, q, k, v, g, slot_idx=None, out_dtype=None) -> o
     gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None,
                   want_dS0=False)                             -> (dq, dk, dv, dg, dS0)
+    gla_conv1d_silu(x, w, bias=None, conv_state=None, slot_idx=None,
+                    init_from_state=False, cu_seqlens=None, max_seqlen=None,
+                    out_dtype=None)                            -> y
     gla_state_alloc(n_slots, H=16, dk=96, dv=192)             -> StatePool
     gla_workspace_size(op, dims)                              -> int
 
@@ -28,6 +31,7 @@ import torch
 
 __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDims",
            "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
+           "gla_conv1d_silu",
            "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS"]
 
 GLA_F32, GLA_BF16 = 0, 1
@@ -37,8 +41,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_INVALID_ARGUMENT", 2: "GLA_ERR_UNSUPPORTED",
           3: "GLA_ERR_OUT_OF_MEMORY", 4: "GLA_ERR_DEVICE"}
 EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slots",
            "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
-           "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd", "gla_status_str",
-           "gla_last_error"]
+           "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd", "gla_conv1d_silu",
+           "gla_status_str", "gla_last_error"]
 
 
 class GlaError(RuntimeError):
@@ -84,11 +88,12 @@ def lib():
     L.gla_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GlaDims), I64, P, P, P, P, P, P, P, I32, P, P, SZ, P]
     L.gla_recurrent_step.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
     L.gla_chunk_bwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.gla_conv1d_silu.argtypes = [I64, I64, I32, I32, I32, P, I64, P, P, P, P, P, I32, P, P]
     L.gla_status_str.argtypes = [I32]
     L.gla_status_str.restype = ctypes.c_char_p
     L.gla_last_error.restype = ctypes.c_char_p
     for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd",
-                 "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd"):
+                 "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd", "gla_conv1d_silu"):
         getattr(L, name).restype = I32
     _LIB = L
     return L
@@ -243,6 +248,48 @@ def gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None, want_dS0=F
                                _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                _ptr(dS0), _ptr(ws), nbytes, _stream()))
     return dq, dk, dv, dg, dS0
+
+
+def gla_conv1d_silu(x, w, bias=None, conv_state=None, slot_idx=None, init_from_state=False,
+                    cu_seqlens=None, max_seqlen=None, out_dtype=None, y=None):
+    """Causal depth-wise convolution of width 4 with SiLU.
+
+    x [B,T,D] (or [N,D] with int32 cu_seqlens [n_seq+1] on the device and
+    max_seqlen); w [D,4] float32; bias [D] float32 or None; conv_state
+    [n_slots,3,D] in x's dtype or None (each sequence's history, updated in
+    place); slot_idx int32 [n_seq] on the device or None.  Returns y.
+    """
+    dev = x.device
+    in_code = _dtype_code(x.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    D = x.shape[-1]
+    if cu_seqlens is None:
+        if x.dim() != 3:
+            raise ValueError("x must be [B, T, D] without cu_seqlens")
+        B, T = x.shape[0], x.shape[1]
+        total = B * T
+    else:
+        if x.dim() != 2 or max_seqlen is None:
+            raise ValueError("x must be [N, D] with cu_seqlens, and max_seqlen must be given")
+        B, T, total = cu_seqlens.numel() - 1, int(max_seqlen), x.shape[0]
+        _need(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32, dev)
+    _need(x, "x", tuple(x.shape), x.dtype, dev)
+    _need(w, "w", (D, 4), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (D,), torch.float32, dev)
+    if conv_state is not None:
+        if conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (3, D):
+            raise ValueError(f"conv_state must be [n_slots, 3, {D}]")
+        _need(conv_state, "conv_state", tuple(conv_state.shape), x.dtype, dev)
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", (B,), torch.int32, dev)
+    if y is None:
+        y = torch.empty(tuple(x.shape), dtype=_torch_dtype(out_code), device=dev)
+    _need(y, "y", tuple(x.shape), _torch_dtype(out_code), dev)
+    _check(lib().gla_conv1d_silu(B, T, D, in_code, out_code, _ptr(cu_seqlens), total, _ptr(x), _ptr(w),
+                                 _ptr(bias), _ptr(conv_state), _ptr(slot_idx), int(bool(init_from_state)),
+                                 _ptr(y), _stream()))
+    return y
 
 
 class StatePool:

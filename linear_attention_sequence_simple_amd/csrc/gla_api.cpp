@@ -503,6 +503,53 @@ gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv, int3
                     "gla_recurrent_step launch");
 }
 
+gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, int32_t out_dtype,
+                           const int32_t* cu_seqlens, int64_t total_tokens, const void* x, const float* w,
+                           const float* bias, void* conv_state, const int32_t* slot_idx, int32_t init_from_state,
+                           void* y, void* stream) {
+  if (B < 1 || T < 1) return fail(GLA_ERR_INVALID_ARGUMENT, "B and T must be >= 1 (got B=%lld, T=%lld)",
+                                  (long long)B, (long long)T);
+  if (D < 8 || D % 8 != 0 || D > (1 << 16))
+    return fail(GLA_ERR_UNSUPPORTED, "D must be a multiple of 8 in [8, 65536] (got %d)", D);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GLA_ERR_INVALID_ARGUMENT, "in_dtype/out_dtype must be GLA_F32 or GLA_BF16");
+  if (cu_seqlens) {
+    if ((uintptr_t)cu_seqlens & 3u) return fail(GLA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+    if (total_tokens < 0 || total_tokens > INT32_MAX)
+      return fail(GLA_ERR_INVALID_ARGUMENT, "total_tokens must be in [0, 2^31) (got %lld)", (long long)total_tokens);
+  } else if (B > INT64_MAX / T) {
+    return fail(GLA_ERR_UNSUPPORTED, "B*T too large");
+  }
+  const int64_t runs = (T + 31) / 32;
+  if (B > ((int64_t)1 << 40) / (runs * (D / 8))) return fail(GLA_ERR_UNSUPPORTED, "B*T*D too large");
+  if (init_from_state != 0 && init_from_state != 1)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_state must be 0 or 1 (got %d)", init_from_state);
+  if (init_from_state && !conv_state)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_state needs conv_state");
+  TRY(check_ptr(x, "x", false));
+  TRY(check_ptr(w, "w", false));
+  TRY(check_ptr(bias, "bias", true));
+  TRY(check_ptr(conv_state, "conv_state", true));
+  if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
+  TRY(check_ptr(y, "y", false));
+  ConvArgs a{};
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.state = conv_state;
+  a.slot = slot_idx;
+  a.cu = cu_seqlens;
+  a.B = B;
+  a.T = T;
+  a.total = cu_seqlens ? total_tokens : B * T;
+  a.D = D;
+  a.runs = (int)runs;
+  a.init = init_from_state;
+  a.y = y;
+  return device_err(launch_conv(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream),
+                    "gla_conv1d_silu launch");
+}
+
 gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
                          const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dv, float* dg,
                          float* dS0, void* ws, size_t ws_bytes, void* stream) {

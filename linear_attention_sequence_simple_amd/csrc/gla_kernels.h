@@ -83,6 +83,22 @@ hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, cons
                            int64_t BH, int nseg, int rev, hipStream_t st);
 
 // Decode step: see gla_step.hip.
+// The convolution ahead of the mixer (gla_conv.hip): sequence b is rows
+// cu[b]..cu[b+1] of x (cu null: rows b*T..(b+1)*T), at most T tokens; its
+// history (when state is set) is rows [3] of slot slot[b] (slot null: b).
+struct ConvArgs {
+  const void* x;
+  const float* w;       // [D, 4]
+  const float* bias;    // [D] or null
+  void* state;          // [slots, 3, D] in the input dtype, or null
+  const int32_t* slot;
+  const int32_t* cu;
+  int64_t B, T, total;
+  int D, runs, init;
+  void* y;
+};
+hipError_t launch_conv(const ConvArgs& a, bool in_bf16, bool out_bf16, hipStream_t st);
+
 struct StepArgs {
   const void* q; const void* k; const void* v; const float* g;
   float* pool; const int32_t* slot_idx; void* o;

@@ -114,3 +114,20 @@ def test_packed_prefill_validation(L):
     assert call(10, p, None) == 1 and "pool" in L.gla_last_error().decode()
     bad = gla.GlaDims(B=2, T=0, H=16, dk=96, dv=192, chunk=128, in_dtype=1, out_dtype=1)
     assert L.gla_chunk_fwd_varlen(ctypes.byref(bad), 10, p, p, p, p, p, p, None, 0, p, None, 0, None) == 1
+
+
+def test_conv_validation(L):
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    call = lambda B=2, T=5, D=64, x=p, w=p, state=None, init=0, cu=None, total=0, bias=None: L.gla_conv1d_silu(
+        B, T, D, 1, 1, cu, total, x, w, bias, state, None, init, p, None)
+    assert call(B=0) == 1
+    assert call(T=0) == 1
+    assert call(D=60) == 2 and "multiple of 8" in L.gla_last_error().decode()
+    assert call(D=0) == 2
+    assert call(x=None) == 1 and "x must not be NULL" in L.gla_last_error().decode()
+    assert call(w=ctypes.c_void_p(0x10004)) == 1 and "aligned" in L.gla_last_error().decode()
+    assert call(init=1) == 1 and "conv_state" in L.gla_last_error().decode()
+    assert call(init=2, state=p) == 1
+    assert call(cu=ctypes.c_void_p(0x10002), total=10) == 1 and "cu_seqlens" in L.gla_last_error().decode()
+    assert call(cu=p, total=-1) == 1 and "total_tokens" in L.gla_last_error().decode()
+    assert call(bias=ctypes.c_void_p(0x10008)) == 1 and "bias" in L.gla_last_error().decode()
