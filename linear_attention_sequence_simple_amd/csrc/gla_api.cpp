@@ -520,8 +520,7 @@ gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, in
   } else if (B > INT64_MAX / T) {
     return fail(GLA_ERR_UNSUPPORTED, "B*T too large");
   }
-  const int64_t runs = (T + 31) / 32;
-  if (B > ((int64_t)1 << 40) / (runs * (D / 8))) return fail(GLA_ERR_UNSUPPORTED, "B*T*D too large");
+  if (B > ((int64_t)1 << 36) / (T * (D / 8))) return fail(GLA_ERR_UNSUPPORTED, "B*T*D too large");
   if (init_from_state != 0 && init_from_state != 1)
     return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_state must be 0 or 1 (got %d)", init_from_state);
   if (init_from_state && !conv_state)
@@ -543,7 +542,6 @@ gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, in
   a.T = T;
   a.total = cu_seqlens ? total_tokens : B * T;
   a.D = D;
-  a.runs = (int)runs;
   a.init = init_from_state;
   a.y = y;
   return device_err(launch_conv(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream),

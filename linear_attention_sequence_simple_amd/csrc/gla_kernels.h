@@ -94,7 +94,7 @@ struct ConvArgs {
   const int32_t* slot;
   const int32_t* cu;
   int64_t B, T, total;
-  int D, runs, init;
+  int D, runs, init;    // runs: token runs per sequence, set by the launcher
   void* y;
 };
 hipError_t launch_conv(const ConvArgs& a, bool in_bf16, bool out_bf16, hipStream_t st);
