@@ -128,6 +128,33 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k,
                          float* S_T, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Element strides of a token tensor: element i of the row of (batch b, token
+ * t, head h) is at p[b*batch + t*token + h*head + i] (each row contiguous).
+ * For g, which has one float per (b, t, h), the same with i = 0. */
+typedef struct {
+  int64_t batch, token, head;
+} gla_strides;
+
+/* gla_chunk_fwd over strided views, so that q, k, v (and g) can be read in
+ * place from the output of the fused projection that produces them (a
+ * 9,216-wide row per token holding every head's query, key, value and gate:
+ * "Diseño esencial de Laplace 3B"), and o written into a wider buffer.
+ *   sq, sk, sv, so : strides of q, k, v, o (NULL: the dense [B,T,H,d] layout)
+ *   sg   : strides of g (NULL: dense [B,T,H])
+ * Strides are positive; for q, k, v and o they are multiples of 16 bytes, and
+ * token and head strides times 32 rows stay under 2^31 bytes
+ * (INVALID_ARGUMENT otherwise).  Views must not overlap o or S_T (caller
+ * contract).  Everything else is as gla_chunk_fwd, whose workspace size
+ * applies. */
+gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
+                                 const gla_strides* sq, const void* k,
+                                 const gla_strides* sk, const void* v,
+                                 const gla_strides* sv, const float* g,
+                                 const gla_strides* sg, const float* S0, void* o,
+                                 const gla_strides* so, float* S_T, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Prefill of a batch of sequences of different lengths, packed along one
  * token axis, with the states kept in a pool slot per sequence: the serving
  * layout in which a wrapper ties each sequence's recurrent state to the

@@ -5,6 +5,8 @@ stream, every step of the computation runs in the library's kernels.  The
 functions carry the names of the C entry points (include/gla.h):
 
     gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None)        -> (o, S_T)
+    gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, o=None)
+                                                               -> (o, S_T)
     gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool,
                          slot_idx=None, init_from_pool=False,
                          out_dtype=None)                       -> o
@@ -30,7 +32,7 @@ import os
 import torch
 
 __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDims",
-           "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
+           "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_conv1d_silu",
            "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS"]
 
@@ -41,8 +43,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_INVALID_ARGUMENT", 2: "GLA_ERR_UNSUPPORTED",
           3: "GLA_ERR_OUT_OF_MEMORY", 4: "GLA_ERR_DEVICE"}
 EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slots",
            "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
-           "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd", "gla_conv1d_silu",
-           "gla_status_str", "gla_last_error"]
+           "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
+           "gla_conv1d_silu", "gla_status_str", "gla_last_error"]
 
 
 class GlaError(RuntimeError):
@@ -55,6 +57,10 @@ class GlaDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class GlaStrides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("token", ctypes.c_int64), ("head", ctypes.c_int64)]
 
 
 _LIB = None
@@ -85,6 +91,8 @@ def lib():
     L.gla_state_slot_bytes.restype = SZ
     L.gla_workspace_size.argtypes = [I32, ctypes.POINTER(GlaDims), ctypes.POINTER(SZ)]
     L.gla_chunk_fwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, SZ, P]
+    SP = ctypes.POINTER(GlaStrides)
+    L.gla_chunk_fwd_strided.argtypes = [ctypes.POINTER(GlaDims), P, SP, P, SP, P, SP, P, SP, P, P, SP, P, P, SZ, P]
     L.gla_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GlaDims), I64, P, P, P, P, P, P, P, I32, P, P, SZ, P]
     L.gla_recurrent_step.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
     L.gla_chunk_bwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -93,7 +101,8 @@ def lib():
     L.gla_status_str.restype = ctypes.c_char_p
     L.gla_last_error.restype = ctypes.c_char_p
     for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd",
-                 "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd", "gla_conv1d_silu"):
+                 "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
+                 "gla_conv1d_silu"):
         getattr(L, name).restype = I32
     _LIB = L
     return L
@@ -180,6 +189,50 @@ def gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspac
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gla_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
                                _ptr(o), _ptr(S_T), _ptr(ws), nbytes, _stream()))
+    return o, S_T
+
+
+def _view_strides(t, name, shape, dtype, device):
+    """Strides of a [B,T,H,d] (or [B,T,H]) view whose rows are contiguous."""
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    st = t.stride()
+    if len(shape) == 4 and st[3] != 1:
+        raise ValueError(f"{name} rows must be contiguous (last stride 1)")
+    return GlaStrides(st[0], st[1], st[2])
+
+
+def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspace=None, o=None,
+                          S_T=None):
+    """gla_chunk_fwd on views with any positive batch/token/head strides (for
+    example q, k, v sliced out of a fused projection output), rows contiguous."""
+    B, T, H, _ = q.shape
+    dev = q.device
+    in_code = _dtype_code(q.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    sq = _view_strides(q, "q", (B, T, H, DK), q.dtype, dev)
+    sk = _view_strides(k, "k", (B, T, H, DK), q.dtype, dev)
+    sv = _view_strides(v, "v", (B, T, H, DV), q.dtype, dev)
+    sg = _view_strides(g, "g", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, DK, DV), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, DV), dtype=_torch_dtype(out_code), device=dev)
+    so = _view_strides(o, "o", (B, T, H, DV), _torch_dtype(out_code), dev)
+    if want_state and S_T is None:
+        S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need(S_T, "S_T", (B, H, DK, DV), torch.float32, dev)
+    dims = _dims(B, T, H, in_code, out_code)
+    ws = _workspace(gla_workspace_size(GLA_OP_FWD, dims), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    r = ctypes.byref
+    _check(lib().gla_chunk_fwd_strided(r(dims), _ptr(q), r(sq), _ptr(k), r(sk), _ptr(v), r(sv), _ptr(g), r(sg),
+                                       _ptr(S0), _ptr(o), r(so), _ptr(S_T), _ptr(ws), nbytes, _stream()))
     return o, S_T
 
 

@@ -287,6 +287,32 @@ BwdPlan plan_bwd(const gla_dims* d) {
   return p;
 }
 
+// A view with caller strides (elements), in dv-slices of `slice_w` columns.
+TokView strided_view(const void* p, const gla_strides& s, int slice_w) {
+  TokView v;
+  v.p = p;
+  v.sb = s.batch;
+  v.sh = s.head;
+  v.st = s.token;
+  v.ss = slice_w;
+  return v;
+}
+
+// Strides of a view: 16-byte rows steps, positive, and 32 token rows within
+// the 32-bit tile offsets of the walks.
+gla_status check_strides(const gla_strides* s, size_t esize, bool rows16, const char* name) {
+  if (!s) return GLA_OK;
+  if (s->batch < 1 || s->token < 1 || s->head < 1)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "%s strides must be positive (got %lld, %lld, %lld)", name,
+                (long long)s->batch, (long long)s->token, (long long)s->head);
+  const int64_t q = rows16 ? (int64_t)(16 / esize) : 1;
+  if (s->batch % q || s->token % q || s->head % q)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "%s strides must be multiples of 16 bytes", name);
+  const int64_t lim = ((int64_t)1 << 31) / (32 * (int64_t)esize);
+  if (s->token >= lim || s->head >= lim) return fail(GLA_ERR_INVALID_ARGUMENT, "%s strides too large", name);
+  return GLA_OK;
+}
+
 // The forward's walk arguments over [B,T,H,cols] tensors (T of dims), with
 // sequences of at most max_len tokens.
 WalkArgs fwd_args(const gla_dims* dims, const FwdPlan& p, const void* q, const void* k, const void* v,
@@ -430,6 +456,43 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, con
   const hipError_t e = run_fwd(dims, p, a, state_plain(const_cast<float*>(S0), w), state_plain(S_T, w), ws,
                                (hipStream_t)stream);
   return device_err(e, "gla_chunk_fwd launch");
+}
+
+gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q, const gla_strides* sq, const void* k,
+                                 const gla_strides* sk, const void* v, const gla_strides* sv, const float* g,
+                                 const gla_strides* sg, const float* S0, void* o, const gla_strides* so,
+                                 float* S_T, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(dims));
+  TRY(check_ptr(q, "q", false));
+  TRY(check_ptr(k, "k", false));
+  TRY(check_ptr(v, "v", false));
+  if (!g || ((uintptr_t)g & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "g must be a non-NULL, 4-byte aligned pointer");
+  TRY(check_ptr(S0, "S0", true));
+  TRY(check_ptr(o, "o", false));
+  TRY(check_ptr(S_T, "S_T", true));
+  const size_t isz = dims->in_dtype == GLA_BF16 ? 2 : 4, osz = dims->out_dtype == GLA_BF16 ? 2 : 4;
+  TRY(check_strides(sq, isz, true, "q"));
+  TRY(check_strides(sk, isz, true, "k"));
+  TRY(check_strides(sv, isz, true, "v"));
+  TRY(check_strides(so, osz, true, "o"));
+  TRY(check_strides(sg, 4, false, "g"));
+  const FwdPlan p = plan_fwd(dims);
+  if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
+  if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  WalkArgs a = fwd_args(dims, p, q, k, v, g, o, dims->T);
+  const int w = DV / p.ns;
+  if (sq) a.Q = strided_view(q, *sq, 0);
+  if (sk) a.X = strided_view(k, *sk, 0);
+  if (sv) a.Y = strided_view(v, *sv, w);
+  if (so) a.O = strided_view(o, *so, w);
+  if (sg) {
+    a.gsb = sg->batch;
+    a.gst = sg->token;
+    a.gsh = sg->head;
+  }
+  const hipError_t e = run_fwd(dims, p, a, state_plain(const_cast<float*>(S0), w), state_plain(S_T, w), ws,
+                               (hipStream_t)stream);
+  return device_err(e, "gla_chunk_fwd_strided launch");
 }
 
 gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens, const void* q,

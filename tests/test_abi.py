@@ -131,3 +131,19 @@ def test_conv_validation(L):
     assert call(cu=ctypes.c_void_p(0x10002), total=10) == 1 and "cu_seqlens" in L.gla_last_error().decode()
     assert call(cu=p, total=-1) == 1 and "total_tokens" in L.gla_last_error().decode()
     assert call(bias=ctypes.c_void_p(0x10008)) == 1 and "bias" in L.gla_last_error().decode()
+
+
+def test_strided_validation(L):
+    d = dims()
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    S = gla.GlaStrides
+    dense_q = S(300 * 16 * 96, 16 * 96, 96)
+    call = lambda sq=None, sg=None, so=None, g=p: L.gla_chunk_fwd_strided(
+        ctypes.byref(d), p, sq and ctypes.byref(sq), p, None, p, None, g, sg and ctypes.byref(sg), None, p,
+        so and ctypes.byref(so), None, None, 0, None)
+    assert call(sq=S(0, 96, 96)) == 1 and "positive" in L.gla_last_error().decode()
+    assert call(sq=S(9216 * 300, 9216, 100)) == 1 and "16 bytes" in L.gla_last_error().decode()
+    assert call(sq=S(1 << 40, 1 << 30, 96)) == 1 and "too large" in L.gla_last_error().decode()
+    assert call(so=S(-1, 192, 192)) == 1
+    assert call(g=ctypes.c_void_p(0x10002)) == 1 and "g must be" in L.gla_last_error().decode()
+    assert call(sq=dense_q, sg=S(300 * 17, 17, 0)) == 1 and "g strides" in L.gla_last_error().decode()
