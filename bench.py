@@ -13,6 +13,8 @@ resident in HBM.  The same line carries, measured in the same run:
   long_context  prefill B=1, T=65536 with a non-zero initial state
   packed    serving prefill: 16 prompts of 2,048-8,192 tokens packed along
             one token axis, final states written into a 1,280-slot pool
+  fused     the headline prefill reading q, k, v in place from the fused
+            [8, 2048, 9216] projection output (strided views, no copies)
   conv      causal depth-wise conv1d (width 4) + SiLU ahead of the mixer,
             B=8, T=2048, D=3,072, bf16 in/out, history kept per sequence
   fp32      prefill B=1, T=2048 with fp32 inputs and outputs
@@ -258,6 +260,28 @@ def bench_packed(torch, gla, steps, warmup):
             "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "bytes": nbytes}
 
 
+def bench_fused(torch, gla, steps, warmup):
+    """The headline prefill on views of one [B, T, 9216] buffer holding every
+    head's q, k, v and gate per token (blocked by projection)."""
+    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=0)
+    B, T = d["meta"]["B"], d["meta"]["T"]
+    dev = torch.device("cuda", 0)
+    buf = torch.zeros((B, T, H * (2 * DK + 2 * DV)), dtype=torch.bfloat16, device=dev)
+    views = (buf[..., :H * DK].unflatten(-1, (H, DK)), buf[..., H * DK:2 * H * DK].unflatten(-1, (H, DK)),
+             buf[..., 2 * H * DK:2 * H * DK + H * DV].unflatten(-1, (H, DV)))
+    for view, name in zip(views, ("q", "k", "v")):
+        view.copy_(torch.from_numpy(d[name]).to(dev).to(torch.bfloat16))
+    g = torch.from_numpy(d["g"]).to(dev)
+    o = torch.empty((B, T, H, DV), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    fn = lambda: gla.gla_chunk_fwd_strided(*views, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T)
+    ms, _ = _time_calls(torch, fn, steps, warmup)
+    nbytes = fwd_bytes(B, T, 2, 2)
+    return {"workload": f"prefill B={B} T={T} H=16 bf16 in/out, q, k, v read in place from a [{B}, {T}, 9216] "
+                        "fused projection buffer", "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
     """The convolution ahead of the mixer.  Its 201 MB per call would stay in
     the 256 MB last-level cache between repeated calls, so the timed calls
@@ -396,7 +420,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "conv", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "conv", "fused", "copy"],
+                    default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -417,6 +442,8 @@ def main():
             print(json.dumps(bench_packed(torch, gla, args.steps, args.warmup)))
         elif args.only == "conv":
             print(json.dumps(bench_conv(torch, gla, args.steps, args.warmup)))
+        elif args.only == "fused":
+            print(json.dumps(bench_fused(torch, gla, args.steps, args.warmup)))
         else:
             n = 1 << 28
             a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -444,6 +471,8 @@ def main():
                               max(3, args.steps // 2), 2)
     packed = bench_packed(torch, gla, max(3, args.steps // 2), 2)
     print(f"[bench] packed {packed['ms']:.4f} ms", file=sys.stderr, flush=True)
+    fused = bench_fused(torch, gla, args.steps, args.warmup)
+    print(f"[bench] fused {fused['ms']:.4f} ms", file=sys.stderr, flush=True)
     conv = bench_conv(torch, gla, max(3, args.steps // 2), 2)
     print(f"[bench] conv {conv['ms']:.4f} ms", file=sys.stderr, flush=True)
     out = {
@@ -460,7 +489,7 @@ def main():
         "mfma_util": {"value": pre["mfma_util"], "algorithmic_flop_per_step": pre["flops"],
                       "peak": "bf16 dense 2500 TFLOP/s",
                       "note": "dense 128-token chunks; the HBM roof caps this at ~0.40 for this workload"},
-        "decode": dec, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed, "conv": conv,
+        "decode": dec, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed, "fused": fused, "conv": conv,
         "parity": {"prefill": pre.get("parity")},
         "cpu_baseline": cpu,
         "kernel_source_digest": src_digest(),
