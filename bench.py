@@ -23,8 +23,8 @@ resident in HBM.  The same line carries, measured in the same run:
   parity    sampled max|err|/rms(ref) against the oracle for this run
 
 --only PART runs a single part a few times (for profiler counter passes):
-prefill | decode | backward | packed | conv | copy (a plain 1 GiB device copy
-used to scale the HBM byte counters).
+prefill | decode | backward | packed | conv | fused | long | copy (a plain
+1 GiB device copy used to scale the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -424,7 +424,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "conv", "fused", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "conv", "fused", "long", "copy"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -448,6 +448,9 @@ def main():
             print(json.dumps(bench_conv(torch, gla, args.steps, args.warmup)))
         elif args.only == "fused":
             print(json.dumps(bench_fused(torch, gla, args.steps, args.warmup)))
+        elif args.only == "long":
+            print(json.dumps(bench_prefill_other(torch, gla, "fwd_bf16_b1_t65536", torch.bfloat16, torch.bfloat16,
+                                                 args.steps, args.warmup)))
         else:
             n = 1 << 28
             a = torch.ones(n, dtype=torch.float32, device="cuda")

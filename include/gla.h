@@ -143,9 +143,9 @@ typedef struct {
  *   sg   : strides of g (NULL: dense [B,T,H])
  * Strides are positive; for q, k, v and o they are multiples of 16 bytes, and
  * token and head strides times 32 rows stay under 2^31 bytes
- * (INVALID_ARGUMENT otherwise).  Views must not overlap o or S_T (caller
- * contract).  Everything else is as gla_chunk_fwd, whose workspace size
- * applies. */
+ * (INVALID_ARGUMENT otherwise).  q, k, v and o are 16-byte aligned, g 4-byte
+ * aligned.  Views must not overlap o or S_T (caller contract).  Everything
+ * else is as gla_chunk_fwd, whose workspace size applies. */
 gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
                                  const gla_strides* sq, const void* k,
                                  const gla_strides* sk, const void* v,
