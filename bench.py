@@ -153,19 +153,30 @@ def _dev_inputs(torch, d, in_dtype):
             T(d["S0"], torch.float32), T(d.get("dO"), in_dtype))
 
 
-def _time_calls(torch, fn, steps, warmup):
+def _time_calls(torch, fn, steps, warmup, warm_ms=0.0):
     """Mean device time per call of fn(): HIP events on the current stream
     bracket the `steps` timed calls, which run back to back.
 
-    A spin of the device is queued ahead of the timed region, so the host-side
-    argument marshalling of the binding never leaves the device idle between
-    calls; the events themselves sit outside the calls, so nothing is inserted
-    between the kernels being timed.  Returns (ms per call, wall seconds)."""
+    The GPU's clocks take some 30 ms of sustained load to reach their steady
+    level: `warmup` untimed calls run first, then (warm_ms > 0, for the parts
+    measured after the host has prepared their inputs) more untimed calls
+    until warm_ms of them have run.  A short spin of the device (about 0.4 ms)
+    is queued ahead of the timed region so that the binding's host-side
+    marshalling (some 14 us per call, below every kernel's duration) never
+    leaves the device idle; a longer spin lets the clocks drop again.  The
+    events sit outside the calls, so nothing is inserted between the kernels
+    being timed.  Returns (ms per call, wall seconds)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if warm_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warm_ms:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(steps * 5e5))             # ~0.2 ms of queue per call at 2.4 GHz
+    torch.cuda._sleep(int(1e6))
     t0 = time.perf_counter()
     e0.record()
     for _ in range(steps):
@@ -222,7 +233,7 @@ def bench_prefill_other(torch, gla, name, in_dtype, out_dtype, steps, warmup):
     o = torch.empty((B, T, H, DV), dtype=out_dtype, device=q.device)
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=q.device)
     fn = lambda: gla.gla_chunk_fwd(q, k, v, g, S0, out_dtype=out_dtype, o=o, S_T=S_T, workspace=ws)
-    ms, _ = _time_calls(torch, fn, steps, warmup)
+    ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
     ib = 2 if in_dtype == torch.bfloat16 else 4
     ob = 2 if out_dtype == torch.bfloat16 else 4
     nbytes = fwd_bytes(B, T, ib, ob, s0=S0 is not None)
@@ -252,7 +263,7 @@ def bench_packed(torch, gla, steps, warmup):
     ws = torch.empty(max(gla.gla_workspace_size(gla.GLA_OP_FWD, dims), 1), dtype=torch.uint8, device=dev)
     fn = lambda: gla.gla_chunk_fwd_varlen(q, k, v, g, cu, w["len_hi"], pool, slots, init_from_pool=False,
                                           out_dtype=torch.bfloat16, workspace=ws, o=o)
-    ms, _ = _time_calls(torch, fn, steps, warmup)
+    ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
     pool.free()
     nbytes = packed_bytes(N, n_seq, 2, 2)
     flops = FWD_FLOP_PER_TH * N * H
@@ -279,7 +290,7 @@ def bench_fused(torch, gla, steps, warmup):
     o = torch.empty((B, T, H, DV), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
     fn = lambda: gla.gla_chunk_fwd_strided(*views, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T)
-    ms, _ = _time_calls(torch, fn, steps, warmup)
+    ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
     nbytes = fwd_bytes(B, T, 2, 2)
     return {"workload": f"prefill B={B} T={T} H=16 bf16 in/out, q, k, v read in place from a [{B}, {T}, 9216] "
                         "fused projection buffer", "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
@@ -304,7 +315,7 @@ def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
         i = it[0] % sets
         it[0] += 1
         gla.gla_conv1d_silu(xs[i], w, bias, conv_state=hist, init_from_state=True, y=ys[i])
-    ms, _ = _time_calls(torch, fn, steps, warmup)
+    ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
     # x read and y written once (2 B each per token-channel), the history read and written
     nbytes = B * T * D * 4 + 2 * B * 3 * D * 2
     return {"workload": f"causal depth-wise conv1d width 4 + SiLU, B={B} T={T} D={D}, bf16 in/out, "
@@ -379,7 +390,7 @@ def bench_backward(torch, gla, steps, warmup):
     dims = gla.GlaDims(B, T, H, DK, DV, CH, gla.GLA_BF16, gla.GLA_BF16)
     ws = torch.empty(gla.gla_workspace_size(gla.GLA_OP_BWD, dims), dtype=torch.uint8, device=q.device)
     fn = lambda: gla.gla_chunk_bwd(q, k, v, g, dO, out_dtype=torch.bfloat16, workspace=ws)
-    ms, _ = _time_calls(torch, fn, steps, warmup)
+    ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
     nbytes = bwd_bytes(B, T, 2, 2)
     flops = BWD_FLOP_PER_TH * B * T * H
     return {"workload": f"backward B={B} T={T} H=16 bf16 in/out, fp32 dg, S0 = dS_T = 0",
@@ -422,8 +433,8 @@ def traffic_from_profiles():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "conv", "fused", "long", "copy"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
