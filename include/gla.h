@@ -166,7 +166,8 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
  *   dims        : B = number of sequences, T = an upper bound of every
  *                 sequence's length (it sizes the launch plan and the
  *                 workspace), H, dk, dv, chunk and dtypes as for gla_chunk_fwd
- *   total_tokens: rows of the packed tensors, < 2^31
+ *   total_tokens: rows of the packed tensors, < 2^31 (0: every sequence is
+ *                 empty, and q, k, v, g and o may be NULL)
  *   cu_seqlens  : device int32 [B + 1]; sequence b is rows
  *                 [cu_seqlens[b], cu_seqlens[b+1]).  Non-decreasing, within
  *                 [0, total_tokens], lengths <= T (caller contract: the

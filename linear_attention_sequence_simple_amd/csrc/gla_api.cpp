@@ -514,11 +514,12 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
                 (long long)pool->n_slots);
   if (init_from_pool != 0 && init_from_pool != 1)
     return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_pool must be 0 or 1 (got %d)", init_from_pool);
-  TRY(check_ptr(q, "q", false));
-  TRY(check_ptr(k, "k", false));
-  TRY(check_ptr(v, "v", false));
-  TRY(check_ptr(g, "g", false));
-  TRY(check_ptr(o, "o", false));
+  const bool no_tokens = total_tokens == 0;      // every sequence empty: token tensors may be NULL
+  TRY(check_ptr(q, "q", no_tokens));
+  TRY(check_ptr(k, "k", no_tokens));
+  TRY(check_ptr(v, "v", no_tokens));
+  TRY(check_ptr(g, "g", no_tokens));
+  TRY(check_ptr(o, "o", no_tokens));
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));

@@ -147,3 +147,10 @@ def test_strided_validation(L):
     assert call(so=S(-1, 192, 192)) == 1
     assert call(g=ctypes.c_void_p(0x10002)) == 1 and "g must be" in L.gla_last_error().decode()
     assert call(sq=dense_q, sg=S(300 * 17, 17, 0)) == 1 and "g strides" in L.gla_last_error().decode()
+
+
+def test_backward_length_limit(L):
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    d = dims(B=1, T=131_073, H=1)
+    st = L.gla_chunk_bwd(ctypes.byref(d), p, p, p, p, None, p, None, p, p, p, p, None, p, 1 << 40, None)
+    assert st == 2 and "1024 chunks" in L.gla_last_error().decode()

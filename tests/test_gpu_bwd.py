@@ -99,3 +99,15 @@ def test_backward_workload_sampled():
         assert_close(sub(x), y, TOL, name)
     for x in got[:4]:
         assert np.isfinite(x).all()
+
+
+def test_longest_supported_sequence():
+    """T = 131,072, the backward's limit of 1,024 chunks, on one head (the
+    segment plan with every kernel at its largest chunk count)."""
+    d = inputs("bwd_bf16_b4_t4096", seed=12, B=1, T=131_072, H=1, S0="normal0.1", with_dO=True,
+               with_dS_T=True)
+    print("case bwd T=131072", flush=True)
+    got = run_bwd(d)
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], d["S0"], d["dS_T"], ckpt=1024)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dS0"), got, ref):
+        assert_close(x, y, TOL, name)

@@ -187,3 +187,27 @@ def test_serving_prefill_full_size_sampled():
             assert_close(to_np(pool.view()[sl, h]), S_ref[0, 0], TOL_BF16, f"slot {sl} head {h}")
     finally:
         pool.free()
+
+
+@pytest.mark.parametrize("init", [False, True])
+def test_packed_all_sequences_empty(init):
+    """A batch whose sequences are all empty (no tokens at all): the slots of
+    the batch get their initial state (zero, or the slot's own), nothing else
+    changes."""
+    import linear_attention_sequence_simple_amd as gla
+    H = 2
+    pool = gla.gla_state_alloc(4, H=H)
+    st0 = torch.from_numpy(np.random.default_rng(17).standard_normal((4, H, 96, 192)).astype(np.float32)).to(dev())
+    pool.view().copy_(st0)
+    empty = lambda c: torch.empty((0, H, c), dtype=torch.bfloat16, device=dev())
+    o = gla.gla_chunk_fwd_varlen(empty(96), empty(96), empty(192), torch.empty((0, H), device=dev()),
+                                 torch.zeros(3, dtype=torch.int32, device=dev()), 128, pool,
+                                 torch.tensor([3, 1], dtype=torch.int32, device=dev()), init_from_pool=init)
+    torch.cuda.synchronize()
+    got = pool.view().clone()
+    pool.free()
+    assert o.shape == (0, H, 192)
+    want = st0.clone()
+    if not init:
+        want[[3, 1]] = 0
+    assert torch.equal(got, want)
