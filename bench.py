@@ -440,8 +440,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the mixer runs on a single MI355X and this build has no "
-              "multi-GPU path (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library runs the mixer on a single MI355X and has no "
+              "multi-GPU path (every (b, h) is independent, so the prefill, decode and backward would "
+              "shard over batch or heads with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.only:

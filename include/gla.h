@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
   GLA_OK = 0,
   GLA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, workspace too small */
-  GLA_ERR_UNSUPPORTED = 2,      /* a size or dtype this build does not implement */
+  GLA_ERR_UNSUPPORTED = 2,      /* a size or dtype this library does not implement */
   GLA_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed (gla_state_alloc only) */
   GLA_ERR_DEVICE = 4            /* the HIP runtime reported an error at launch */
 } gla_status;
