@@ -19,6 +19,8 @@ resident in HBM.  The same line carries, measured in the same run:
             B=8, T=2048, D=3,072, bf16 in/out, history kept per sequence
   fp32      prefill B=1, T=2048 with fp32 inputs and outputs
   roofline  the prefill walk kernel against the HBM roof (HIP events)
+  hbm_copy_reference  a plain device copy on rotating buffers: the streaming
+            rate this GPU reaches, and each HBM-bound part as a fraction of it
   cpu_baseline  the fp64 oracle on the host cores, whole workload
   parity    sampled max|err|/rms(ref) against the oracle for this run
 
@@ -157,24 +159,24 @@ def _time_calls(torch, fn, steps, warmup, warm_ms=0.0):
     """Mean device time per call of fn(): HIP events on the current stream
     bracket the `steps` timed calls, which run back to back.
 
-    The GPU's clocks take some 30 ms of sustained load to reach their steady
-    level: `warmup` untimed calls run first, then (warm_ms > 0, for the parts
-    measured after the host has prepared their inputs) more untimed calls
-    until warm_ms of them have run.  A short spin of the device (about 0.4 ms)
+    The GPU's clocks take some 50 ms of sustained load to reach their steady
+    level from idle: `warmup` untimed calls run first, then more untimed calls
+    until at least warm_ms of warm-up have passed (the first part measured
+    asks for 100 ms, the parts measured after the host has prepared their
+    inputs for 30 ms).  A short spin of the device (about 0.4 ms)
     is queued ahead of the timed region so that the binding's host-side
     marshalling (some 14 us per call, below every kernel's duration) never
     leaves the device idle; a longer spin lets the clocks drop again.  The
     events sit outside the calls, so nothing is inserted between the kernels
     being timed.  Returns (ms per call, wall seconds)."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    if warm_ms > 0:
-        t0 = time.perf_counter()
-        while (time.perf_counter() - t0) * 1e3 < warm_ms:
-            for _ in range(4):
-                fn()
-            torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(1e6))
     t0 = time.perf_counter()
@@ -203,7 +205,7 @@ def bench_prefill(torch, gla, steps, warmup, parity=True):
     ws_bytes = gla.gla_workspace_size(gla.GLA_OP_FWD, dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     fn = lambda: gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T, workspace=ws)
-    ms, wall = _time_calls(torch, fn, steps, warmup)
+    ms, wall = _time_calls(torch, fn, steps, warmup, warm_ms=100)
     tokens = B * T
     nbytes = fwd_bytes(B, T, 2, 2)
     flops = FWD_FLOP_PER_TH * B * T * H
@@ -324,6 +326,25 @@ def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes, "kernels_per_call": 1}
 
 
+def copy_reference(torch, steps, sets=4, nbytes=100_663_296):
+    """What plain streaming reaches on this GPU: torch's device copy of a
+    100.7 MB tensor (the size of the prefill's o), cycling over `sets`
+    source/destination pairs so that the data comes from HBM."""
+    dev = torch.device("cuda", 0)
+    src = [torch.randn(nbytes // 4, device=dev) for _ in range(sets)]
+    dst = [torch.empty_like(src[0]) for _ in range(sets)]
+    it = [0]
+
+    def fn():
+        i = it[0] % sets
+        it[0] += 1
+        dst[i].copy_(src[i])
+    ms, _ = _time_calls(torch, fn, steps, 0, warm_ms=30)
+    return {"GBps": 2 * nbytes / (ms * 1e-3) / 1e9, "bytes_per_copy": 2 * nbytes,
+            "note": f"torch device-to-device copy of {nbytes} B (read + write), {sets} rotating pairs; "
+                    "a reference point, not a ceiling (the decode's in-place stream runs faster)"}
+
+
 def bench_decode(torch, gla, layers=24, steps=64, warmup=1, parity=True):
     w = gen.WORKLOADS["decode_1280x24x64"]
     n = w["B"]
@@ -434,7 +455,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "packed", "conv", "fused", "long", "copy"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -493,6 +514,7 @@ def main():
     fused = bench_fused(torch, gla, args.steps, args.warmup)
     print(f"[bench] fused {fused['ms']:.4f} ms", file=sys.stderr, flush=True)
     conv = bench_conv(torch, gla, max(3, args.steps // 2), 2)
+    copy = copy_reference(torch, args.steps)
     print(f"[bench] conv {conv['ms']:.4f} ms", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -510,6 +532,9 @@ def main():
                       "note": "dense 128-token chunks; the HBM roof caps this at ~0.40 for this workload"},
         "decode": dec, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed, "fused": fused, "conv": conv,
         "parity": {"prefill": pre.get("parity")},
+        "hbm_copy_reference": dict(copy, prefill_frac_of_copy=pre["GBps"] / copy["GBps"],
+                                   decode_frac_of_copy=dec["GBps"] / copy["GBps"],
+                                   conv_frac_of_copy=conv["GBps"] / copy["GBps"]),
         "cpu_baseline": cpu,
         "kernel_source_digest": src_digest(),
     }
