@@ -53,7 +53,7 @@ H, DK, DV, CH = 16, 96, 192, 128
 
 # Algorithmic work per token-head (dense 128-token chunks):
 #   forward  = 2*C*dk + 2*C*dv + 2*dk*dv + 2*dk*dv = 147,456 flop
-#   backward = 2*C*(3dk + 2dv) + 3*2*dk*dv          = 356,352 flop
+#   backward = 2*C*(3dk + 2dv) + 3*2*dk*dv          = 282,624 flop
 FWD_FLOP_PER_TH = 2 * CH * DK + 2 * CH * DV + 4 * DK * DV
 BWD_FLOP_PER_TH = 2 * CH * (3 * DK + 2 * DV) + 6 * DK * DV
 

@@ -1,0 +1,41 @@
+"""The benchmark's algorithmic byte and flop counts (the numerators of its
+roofline figures), checked against counts made from the tensor shapes."""
+import numpy as np
+
+import bench
+import gen
+
+H, DK, DV, CH = 16, 96, 192, 128
+
+
+def test_prefill_bytes_from_shapes():
+    B, T = 8, 2048
+    q = k = B * T * H * DK * 2          # bf16 inputs
+    v = B * T * H * DV * 2
+    g = B * T * H * 4
+    o = B * T * H * DV * 2              # bf16 output
+    S_T = B * H * DK * DV * 4
+    assert bench.fwd_bytes(B, T, 2, 2) == q + k + v + g + o + S_T == 312_475_648
+    assert bench.fwd_bytes(1, 65536, 2, 2, s0=True) == 1 * 65536 * H * (2 * DK * 2 + DV * 2 + 4 + DV * 2) + 2 * H * DK * DV * 4
+
+
+def test_flops_per_token_head():
+    # dense 128-token chunk: Q K^T (C x dk), P V (C x dv), Q S (dk x dv), K^T V (dk x dv), 2 flops each
+    assert bench.FWD_FLOP_PER_TH == 2 * CH * DK + 2 * CH * DV + 2 * DK * DV + 2 * DK * DV == 147_456
+    # backward: scores and dO V^T (2 C dk + 2 C dv), dq, dk, dv intra (2 C dk + 2 C dk + 2 C dv), three state products
+    assert bench.BWD_FLOP_PER_TH == 2 * CH * (3 * DK + 2 * DV) + 6 * DK * DV == 282_624
+
+
+def test_decode_bytes_from_shapes():
+    n = 1280
+    state = n * H * DK * DV * 4 * 2     # read and written in place
+    io = n * H * (2 * DK * 2 + DV * 2 + 4 + DV * 4)    # bf16 q, k, v; fp32 g; fp32 o
+    assert bench.decode_bytes(n) == state + io
+
+
+def test_packed_bytes_match_the_workload():
+    d = gen.make_packed_inputs("serve_prefill_16x2k8k", seed=0, with_pool=False)
+    N, n_seq = int(d["cu_seqlens"][-1]), len(d["slot_idx"])
+    assert N == int(np.sum(d["meta"]["lengths"])) and n_seq == 16
+    per_token_head = 2 * DK * 2 + DV * 2 + 4 + DV * 2
+    assert bench.packed_bytes(N, n_seq, 2, 2) == N * H * per_token_head + n_seq * H * DK * DV * 4

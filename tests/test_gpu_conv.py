@@ -47,7 +47,7 @@ def _assert_bf16_out(got, ref, name):
 TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "f32"), ("f32", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "f32"), ("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
 def test_conv_batch(in_dt, out_dt):
     import linear_attention_sequence_simple_amd as gla
     B, T, D = 3, 77, 64
