@@ -214,3 +214,13 @@ def test_packed_all_sequences_empty(init):
     if not init:
         want[[3, 1]] = 0
     assert torch.equal(got, want)
+
+
+def test_packed_segments_f32():
+    """fp32 inputs (three dv-slices, the fp32 state walk in pass 1) on the segment plan."""
+    d = gen.make_packed_inputs(seed=18, lengths=[700, 0, 300, 1], n_slots=6, H=2, dtype="f32")
+    o, pool = run_packed(d, torch.float32, torch.float32, True, segments=3)
+    o_ref, pool_ref = oracle.forward_packed(d["q"], d["k"], d["v"], d["g"], d["cu_seqlens"], d["pool"],
+                                            d["slot_idx"], True)
+    assert_close(o, o_ref, TOL_F32, "o")
+    check_pool(pool, pool_ref, d["slot_idx"], TOL_F32, "slots")

@@ -59,7 +59,7 @@ def with_segments(n, fn):
 
 
 @pytest.mark.parametrize("layout", ["blocked", "per_head"])
-@pytest.mark.parametrize("dtype,segments", [("bf16", None), ("bf16", 3), ("f32", None)])
+@pytest.mark.parametrize("dtype,segments", [("bf16", None), ("bf16", 3), ("f32", None), ("f32", 3)])
 def test_fused_layout(layout, dtype, segments):
     import linear_attention_sequence_simple_amd as gla
     B, T = 2, 300
