@@ -23,6 +23,16 @@ is none.  The chunk size (16 chunks of 128 tokens in the Trainium2 rewrite,
 section "Adaptaciones para AWS Trainium2", item 1) does not change the result
 and does not appear here: the oracle walks token by token.
 
+Two more functions follow the same recurrence or sit next to it:
+forward_packed runs `forward` on each sequence of a packed batch from its
+pool slot's state ("AWS serve Laplace 3B di i14 con uno stato fisso di 29,5
+MB", sections "Lo stato di Laplace 3B resta fisso durante l'inferenza" and
+"I risultati dichiarati hanno limiti precisi"), and conv1d_silu is the causal
+depth-wise convolution of width 4 with SiLU that precedes the mixer ("Diseño
+esencial de Laplace 3B").  Every function is pinned by tests that do not
+reuse its formula: tests/test_oracle.py, tests/test_oracle_packed.py and
+tests/test_oracle_conv.py with the fixtures under tests/golden/.
+
 Everything is float64.  Inputs may be any float dtype; callers pass the exact
 values the device sees (bf16 inputs already rounded to bf16).
 
