@@ -189,6 +189,16 @@ def _time_calls(torch, fn, steps, warmup, warm_ms=0.0):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def _bf16_out_ratio(got, ref, tol):
+    """Largest |got - ref| / (tol rms(ref) + 2^-8 |ref|): the elementwise bound
+    for outputs rounded to bf16 (at most 1 passes).  2^-8 |ref| is bf16's half
+    ulp at the bottom of a binade, so rounding alone can bring this close to 1."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = tol * math.sqrt(float(np.mean(ref * ref))) + 2.0 ** -8 * np.abs(ref)
+    return float(np.max(np.abs(got - ref) / bound))
+
+
 def _rel_err(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -266,6 +276,19 @@ def bench_packed(torch, gla, steps, warmup):
     fn = lambda: gla.gla_chunk_fwd_varlen(q, k, v, g, cu, w["len_hi"], pool, slots, init_from_pool=False,
                                           out_dtype=torch.bfloat16, workspace=ws, o=o)
     ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
+    # sampled parity: the longest sequence, head 0, against the oracle (every
+    # call starts from zero, so the slot holds that sequence's final state)
+    import oracle
+    cu_h = d["cu_seqlens"]
+    sb = int(np.argmax(np.diff(cu_h)))
+    t0, t1 = int(cu_h[sb]), int(cu_h[sb + 1])
+    sl = lambda x: x[None, t0:t1, 0:1]
+    o_ref, S_ref = oracle.forward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]))
+    got_o = o[t0:t1, 0].float().cpu().numpy()
+    got_S = pool.view()[int(d["slot_idx"][sb]), 0].cpu().numpy()
+    parity = {"o_bf16_out_over_bound": _bf16_out_ratio(got_o, o_ref[0, :, 0], 1e-2),
+              "slot_state": _rel_err(got_S, S_ref[0, 0]),
+              "sample": f"sequence {sb} ({t1 - t0} tokens), head 0"}
     pool.free()
     nbytes = packed_bytes(N, n_seq, 2, 2)
     flops = FWD_FLOP_PER_TH * N * H
@@ -274,7 +297,7 @@ def bench_packed(torch, gla, steps, warmup):
                         f"({N} in all), H=16 bf16 in/out, final states into a {w['n_slots']}-slot pool",
             "ms": ms, "tokens_per_s": N / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "bytes": nbytes}
+            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "bytes": nbytes, "parity": parity}
 
 
 def bench_fused(torch, gla, steps, warmup):
@@ -293,10 +316,14 @@ def bench_fused(torch, gla, steps, warmup):
     S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
     fn = lambda: gla.gla_chunk_fwd_strided(*views, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T)
     ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
+    o_dense, S_dense = gla.gla_chunk_fwd(*(x.contiguous() for x in views), g, None, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    equal = bool(torch.equal(o, o_dense) and torch.equal(S_T, S_dense))
     nbytes = fwd_bytes(B, T, 2, 2)
     return {"workload": f"prefill B={B} T={T} H=16 bf16 in/out, q, k, v read in place from a [{B}, {T}, 9216] "
                         "fused projection buffer", "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
-            "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "parity": {"bitwise_equal_to_dense_call": equal}}
 
 
 def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
@@ -318,12 +345,23 @@ def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
         it[0] += 1
         gla.gla_conv1d_silu(xs[i], w, bias, conv_state=hist, init_from_state=True, y=ys[i])
     ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
+    # sampled parity: sequence 0 of set 0 from a zero history, against the oracle
+    import oracle
+    hist.zero_()
+    gla.gla_conv1d_silu(xs[0], w, bias, conv_state=hist, init_from_state=True, y=ys[0])
+    torch.cuda.synchronize()
+    x0 = xs[0][0].float().cpu().numpy()
+    y_ref, h_ref = oracle.conv1d_silu(x0, w.cpu().numpy(), bias.cpu().numpy(), [0, T], np.zeros((1, 3, D)), None, True)
+    parity = {"y_bf16_out_over_bound": _bf16_out_ratio(ys[0][0].float().cpu().numpy(), y_ref, 1e-5),
+              "history_bitwise": bool(np.array_equal(hist[0].float().cpu().numpy(), h_ref[0])),
+              "sample": f"sequence 0, all {D} channels, {T} tokens"}
     # x read and y written once (2 B each per token-channel), the history read and written
     nbytes = B * T * D * 4 + 2 * B * 3 * D * 2
     return {"workload": f"causal depth-wise conv1d width 4 + SiLU, B={B} T={T} D={D}, bf16 in/out, "
                         f"history kept per sequence; calls cycle over {sets} input/output sets",
             "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes, "kernels_per_call": 1}
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes, "kernels_per_call": 1,
+            "parity": parity}
 
 
 def copy_reference(torch, steps, sets=4, nbytes=100_663_296):
