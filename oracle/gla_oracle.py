@@ -29,9 +29,13 @@ pool slot's state ("AWS serve Laplace 3B di i14 con uno stato fisso di 29,5
 MB", sections "Lo stato di Laplace 3B resta fisso durante l'inferenza" and
 "I risultati dichiarati hanno limiti precisi"), and conv1d_silu is the causal
 depth-wise convolution of width 4 with SiLU that precedes the mixer ("Diseño
-esencial de Laplace 3B").  Every function is pinned by tests that do not
-reuse its formula: tests/test_oracle.py, tests/test_oracle_packed.py and
-tests/test_oracle_conv.py with the fixtures under tests/golden/.
+esencial de Laplace 3B").  q16_encode, q16_decode and step_q16 hold the
+decode state in 16 bits (an int16 mantissa per element, one power-of-two
+exponent per state column), after the INT16 storage of the HEAL summary
+(section "A. Mitigando o Truncamento de Atenção via Quantização INT16").
+Every function is pinned by tests that do not reuse its formula:
+tests/test_oracle.py, tests/test_oracle_packed.py, tests/test_oracle_conv.py
+and tests/test_oracle_q16.py with the fixtures under tests/golden/.
 
 Everything is float64.  Inputs may be any float dtype; callers pass the exact
 values the device sees (bf16 inputs already rounded to bf16).
@@ -44,7 +48,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "forward_packed", "step", "backward", "conv1d_silu", "state_bytes"]
+__all__ = ["forward", "forward_packed", "step", "backward", "conv1d_silu", "state_bytes",
+           "q16_encode", "q16_decode", "step_q16", "Q16_MAX", "Q16_NAN"]
 
 
 def _f64(x):
@@ -219,6 +224,67 @@ def conv1d_silu(x, w, bias, cu_seqlens, state=None, slot_idx=None, init_from_sta
         if new_state is not None:
             new_state[slots[b]] = z[-3:]
     return y, new_state
+
+
+# ---------------------------------------------------------------------------
+# 16-bit state ("Q16").  The HEAL summary ("Resumo Técnico: Desmistificando a
+# Instabilidade Numérica na Inferência de LLMs com HEAL", section "A.
+# Mitigando o Truncamento de Atenção via Quantização INT16") keeps tensors in
+# 16-bit integers to hold memory at 16 bits per element with less truncation
+# than a 16-bit float, and rescales rare outlier channels to stay in range.
+# Here the decode state is stored that way: every element of column d (a
+# value channel) is an int16 mantissa m with one shared power-of-two
+# exponent e[d], value m * 2^e[d].  e[d] is set from the column's largest
+# magnitude M so that M / 2^e lies in [2^14, 2^15) (one step higher when M
+# would round up to 2^15): the largest entry keeps 15 bits and the rounding
+# error is at most half a quantum 2^e <= 2^-14 M.  Arithmetic stays fp64 here
+# (fp32 on the device); only the stored state is 16-bit.
+
+Q16_MAX = 32767       # largest mantissa magnitude
+Q16_NAN = -32768      # reserved mantissa: the column held a non-finite value
+
+
+def q16_encode(S):
+    """Encode states S [..., dk, dv] as (m int16 [..., dk, dv], e int32 [..., dv]).
+
+    Per column: M = max |S[:, d]|; with M = f 2^x, f in [1/2, 1) (frexp),
+    e = x - 15, so M / 2^e = f 2^15 in [2^14, 2^15), and e = x - 14 when
+    M / 2^(x-15) >= 32767.5 (it would round to 2^15); M = 0 gives e = -15.
+    m = round-half-even(S / 2^e), within +-32767.  A column with a
+    non-finite entry is stored as Q16_NAN throughout with e = 0.
+    """
+    S = _f64(S)
+    finite = np.isfinite(S).all(axis=-2)                       # [..., dv]
+    M = np.where(finite, np.abs(np.where(np.isfinite(S), S, 0.0)).max(axis=-2), 0.0)
+    _, x = np.frexp(M)
+    e = x - 15
+    e = e + (np.ldexp(M, -e) >= Q16_MAX + 0.5)
+    e = np.where(finite, e, 0).astype(np.int32)
+    scaled = np.ldexp(np.where(np.isfinite(S), S, 0.0), -e[..., None, :])
+    m = np.rint(scaled)
+    assert np.all(np.abs(m) <= Q16_MAX)
+    m = np.where(finite[..., None, :], m, Q16_NAN)
+    return m.astype(np.int16), e
+
+
+def q16_decode(m, e):
+    """Values m * 2^e[d] in float64 (NaN where m is Q16_NAN)."""
+    m = np.asarray(m)
+    v = np.ldexp(m.astype(np.float64), np.asarray(e, np.int64)[..., None, :])
+    return np.where(m == Q16_NAN, np.nan, v)
+
+
+def step_q16(m, e, q, k, v, g):
+    """One decode step on 16-bit states.
+
+    m [N, H, dk, dv] int16, e [N, H, dv] int32; q, k [N, H, dk]; v [N, H, dv];
+    g [N, H].  The stored state is decoded, updated as in `step` in float64,
+    the query reads the updated state before it is rounded, and the new state
+    is encoded.  Returns (o [N, H, dv] float64, m_new, e_new).
+    """
+    o, S = step(q16_decode(m, e), q, k, v, g)
+    m_new, e_new = q16_encode(S)
+    return o, m_new, e_new
 
 
 def state_bytes(H, dk, dv, itemsize=4):
