@@ -104,6 +104,53 @@ int64_t gla_state_slots(const gla_state* pool);
 /* Bytes of one slot: H*dk*dv*4. */
 size_t gla_state_slot_bytes(int32_t H, int32_t dk, int32_t dv);
 
+/* ---------------------------------------------------------------------------
+ * 16-bit state pools.  The HEAL summary ("Resumo Técnico: Desmistificando a
+ * Instabilidade Numérica na Inferência de LLMs com HEAL", section "A.
+ * Mitigando o Truncamento de Atenção via Quantização INT16") stores tensors
+ * as 16-bit integers to keep 16 bits per element with less truncation than a
+ * 16-bit float.  A GLA_STATE_Q16 pool stores each state that way: column d
+ * (a value channel) of a [dk, dv] state holds int16 mantissas m[c][d] and one
+ * int32 exponent e[d]; the value is m * 2^e.  e is chosen from the column's
+ * largest magnitude M after every update: with M = f 2^x, f in [1/2, 1),
+ * e = x - 15, one more when M / 2^e >= 32767.5, so M sits at [2^14, 2^15)
+ * quanta and mantissas, rounded half to even, stay within +-32767.  The
+ * rounding error is at most half a quantum, 2^-15 M per column.  A column
+ * holding a non-finite value is stored as mantissa -32768 (reads as NaN).
+ * A slot takes H*(dk*dv*2 + dv*4) bytes: 602,112 B at H=16 against
+ * 1,179,648 B in float32, and the decode step moves half the bytes.
+ */
+typedef enum { GLA_STATE_F32 = 0, GLA_STATE_Q16 = 1 } gla_state_fmt;
+
+/* Allocates a zero-filled 16-bit pool: mantissas [n_slots, H, dk, dv] int16,
+ * then (256-byte aligned) exponents [n_slots, H, dv] int32, in one device
+ * allocation owned by the library; free it with gla_state_free.  Errors as
+ * gla_state_alloc. */
+gla_status gla_state_alloc_q16(int64_t n_slots, int32_t H, int32_t dk, int32_t dv,
+                               void* stream, gla_state** out);
+
+/* GLA_STATE_F32 or GLA_STATE_Q16; -1 for NULL. */
+int32_t gla_state_format(const gla_state* pool);
+
+/* Device pointers to slot `slot` of a 16-bit pool: mantissas [H, dk, dv] and
+ * exponents [H, dv] (gla_state_ptr returns NULL for such pools).
+ * Errors: INVALID_ARGUMENT (NULL arguments, a float32 pool, slot out of range). */
+gla_status gla_state_q16_ptrs(const gla_state* pool, int64_t slot, int16_t** mant,
+                              int32_t** expo);
+
+/* Moves n float32 states S [n, H, dk, dv] (device) into pool slots
+ * slot_idx[i] (device int32 [n]; NULL: slots 0..n-1): a copy for a float32
+ * pool, encoded as above for a 16-bit pool.  gla_state_read is the inverse
+ * (exact for a 16-bit pool: every stored value is a float32).  Asynchronous
+ * on `stream`; slot indices in range and distinct (caller contract).
+ * This is how the float32 final states of a prefill enter a 16-bit pool.
+ * Errors: INVALID_ARGUMENT (NULL pool or S, n < 0, n > slots with slot_idx
+ * NULL, misaligned slot_idx), UNSUPPORTED, DEVICE. */
+gla_status gla_state_write(gla_state* pool, int64_t n, const int32_t* slot_idx,
+                           const float* S, void* stream);
+gla_status gla_state_read(const gla_state* pool, int64_t n, const int32_t* slot_idx,
+                          float* S, void* stream);
+
 /* Workspace bytes that gla_chunk_fwd (op = GLA_OP_FWD) or gla_chunk_bwd
  * (op = GLA_OP_BWD) needs for `dims`.  Same validation as those calls. */
 gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes);
@@ -185,7 +232,9 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
  *   The final state of every sequence is written to its slot.
  *   ws   : at least gla_workspace_size(GLA_OP_FWD, dims) bytes.
  * Errors: as gla_chunk_fwd, plus INVALID_ARGUMENT for a NULL or misaligned
- * cu_seqlens, a pool whose H/dk/dv differ, B > slots with slot_idx NULL.
+ * cu_seqlens, a pool whose H/dk/dv differ, B > slots with slot_idx NULL;
+ * UNSUPPORTED for a 16-bit pool (prefill into float32 states and encode them
+ * with gla_state_write).
  */
 gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens,
                                 const int32_t* cu_seqlens, const void* q,
@@ -197,7 +246,7 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens,
 /* ---------------------------------------------------------------------------
  * Batched single-token decode step, in place on a state pool.  For each of B
  * sequences and each head: S <- exp(g) S + k^T v, then o = q S.  The state
- * stays float32 and the cost per token does not depend on the context length
+ * has a fixed size, so the cost per token does not depend on the context length
  * ("I risultati dichiarati hanno limiti precisi": a longer prompt barely
  * changes the cost per output token; "Resultados de entrenamiento e
  * inferencia": 1,280 concurrent sequences).
@@ -207,6 +256,10 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens,
  *          slot b when slot_idx is NULL.  Indices must be in range and
  *          distinct (caller contract, not checked on the device).
  *   o    : [B, H, dv] out_dtype.
+ * A float32 pool is updated in float32.  A 16-bit pool (gla_state_alloc_q16)
+ * is decoded, updated in float32 the same way, o is read from the updated
+ * float32 values, and the result is encoded again (its rounding affects the
+ * next step, not this o).
  * Errors: INVALID_ARGUMENT (null pointers, B < 1, H or dk/dv differing from
  * the pool's, B > slots when slot_idx is NULL), UNSUPPORTED, DEVICE.
  */

@@ -17,6 +17,10 @@ functions carry the names of the C entry points (include/gla.h):
                     init_from_state=False, cu_seqlens=None, max_seqlen=None,
                     out_dtype=None)                            -> y
     gla_state_alloc(n_slots, H=16, dk=96, dv=192)             -> StatePool
+    gla_state_alloc_q16(n_slots, H=16, dk=96, dv=192)         -> StatePool (16-bit)
+    gla_state_format(pool)                                    -> GLA_STATE_F32 | GLA_STATE_Q16
+    gla_state_write(pool, S, slot_idx=None)                   (float32 states into slots)
+    gla_state_read(pool, n=None, slot_idx=None, S=None)       -> S float32
     gla_workspace_size(op, dims)                              -> int
 
 Layouts: q, k [B,T,H,96]; v, o, dO [B,T,H,192]; g [B,T,H] float32; states
@@ -33,18 +37,21 @@ import torch
 
 __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDims",
            "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
-           "gla_conv1d_silu",
+           "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_write",
+           "gla_state_read", "GLA_STATE_F32", "GLA_STATE_Q16",
            "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS"]
 
 GLA_F32, GLA_BF16 = 0, 1
 GLA_OP_FWD, GLA_OP_BWD = 0, 1
+GLA_STATE_F32, GLA_STATE_Q16 = 0, 1
 CHUNK, DK, DV = 128, 96, 192
 STATUS = {0: "GLA_OK", 1: "GLA_ERR_INVALID_ARGUMENT", 2: "GLA_ERR_UNSUPPORTED",
           3: "GLA_ERR_OUT_OF_MEMORY", 4: "GLA_ERR_DEVICE"}
 EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slots",
            "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
            "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
-           "gla_conv1d_silu", "gla_status_str", "gla_last_error"]
+           "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_q16_ptrs",
+           "gla_state_write", "gla_state_read", "gla_status_str", "gla_last_error"]
 
 
 class GlaError(RuntimeError):
@@ -97,12 +104,19 @@ def lib():
     L.gla_recurrent_step.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
     L.gla_chunk_bwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.gla_conv1d_silu.argtypes = [I64, I64, I32, I32, I32, P, I64, P, P, P, P, P, I32, P, P]
+    L.gla_state_alloc_q16.argtypes = [I64, I32, I32, I32, P, ctypes.POINTER(P)]
+    L.gla_state_format.argtypes = [P]
+    L.gla_state_format.restype = I32
+    L.gla_state_q16_ptrs.argtypes = [P, I64, ctypes.POINTER(P), ctypes.POINTER(P)]
+    L.gla_state_write.argtypes = [P, I64, P, P, P]
+    L.gla_state_read.argtypes = [P, I64, P, P, P]
     L.gla_status_str.argtypes = [I32]
     L.gla_status_str.restype = ctypes.c_char_p
     L.gla_last_error.restype = ctypes.c_char_p
     for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd",
                  "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
-                 "gla_conv1d_silu"):
+                 "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_q16_ptrs", "gla_state_write",
+                 "gla_state_read"):
         getattr(L, name).restype = I32
     _LIB = L
     return L
@@ -345,14 +359,26 @@ def gla_conv1d_silu(x, w, bias=None, conv_state=None, slot_idx=None, init_from_s
     return y
 
 
-class StatePool:
-    """A library-owned float32 pool of recurrent states [n_slots, H, dk, dv]."""
+class _DeviceArray:
+    """A device buffer described for torch.as_tensor (no copy)."""
 
-    def __init__(self, n_slots, H=16, dk=DK, dv=DV):
+    def __init__(self, ptr, shape, typestr):
+        self.__cuda_array_interface__ = {"shape": shape, "typestr": typestr, "data": (ptr, False),
+                                         "version": 3, "strides": None}
+
+
+class StatePool:
+    """A library-owned pool of recurrent states [n_slots, H, dk, dv]: float32
+    (fmt GLA_STATE_F32) or 16-bit mantissas with one exponent per state column
+    (GLA_STATE_Q16)."""
+
+    def __init__(self, n_slots, H=16, dk=DK, dv=DV, fmt=GLA_STATE_F32):
         handle = ctypes.c_void_p()
-        _check(lib().gla_state_alloc(n_slots, H, dk, dv, _stream(), ctypes.byref(handle)))
+        alloc = lib().gla_state_alloc_q16 if fmt == GLA_STATE_Q16 else lib().gla_state_alloc
+        _check(alloc(n_slots, H, dk, dv, _stream(), ctypes.byref(handle)))
         self._h = handle
         self.n_slots, self.H, self.dk, self.dv = n_slots, H, dk, dv
+        self.fmt = lib().gla_state_format(handle)
         self.device = torch.device("cuda", torch.cuda.current_device())
 
     @property
@@ -373,12 +399,25 @@ class StatePool:
 
     @property
     def __cuda_array_interface__(self):
+        if self.fmt != GLA_STATE_F32:
+            raise TypeError("a 16-bit pool has no float32 view: use q16_views() or gla_state_read")
         return {"shape": (self.n_slots, self.H, self.dk, self.dv), "typestr": "<f4",
                 "data": (self.ptr(0), False), "version": 3, "strides": None}
 
     def view(self) -> torch.Tensor:
-        """A torch tensor aliasing the pool (no copy)."""
+        """A torch tensor aliasing a float32 pool (no copy)."""
+        if self.fmt != GLA_STATE_F32:
+            raise TypeError("a 16-bit pool has no float32 view: use q16_views() or gla_state_read")
         return torch.as_tensor(self, device=self.device)
+
+    def q16_views(self):
+        """(mantissas int16 [n_slots,H,dk,dv], exponents int32 [n_slots,H,dv])
+        aliasing a 16-bit pool (no copy)."""
+        m, e = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().gla_state_q16_ptrs(self.handle, 0, ctypes.byref(m), ctypes.byref(e)))
+        mant = _DeviceArray(m.value, (self.n_slots, self.H, self.dk, self.dv), "<i2")
+        expo = _DeviceArray(e.value, (self.n_slots, self.H, self.dv), "<i4")
+        return torch.as_tensor(mant, device=self.device), torch.as_tensor(expo, device=self.device)
 
     def free(self):
         if self._h is not None:
@@ -394,6 +433,38 @@ class StatePool:
 
 def gla_state_alloc(n_slots, H=16, dk=DK, dv=DV) -> StatePool:
     return StatePool(n_slots, H, dk, dv)
+
+
+def gla_state_alloc_q16(n_slots, H=16, dk=DK, dv=DV) -> StatePool:
+    return StatePool(n_slots, H, dk, dv, fmt=GLA_STATE_Q16)
+
+
+def gla_state_format(pool: StatePool) -> int:
+    return lib().gla_state_format(pool.handle)
+
+
+def gla_state_write(pool: StatePool, S, slot_idx=None):
+    """Float32 states S [n,H,dk,dv] into slots slot_idx (int32 [n]) or 0..n-1
+    (encoded for a 16-bit pool)."""
+    n = S.shape[0]
+    _need(S, "S", (n, pool.H, pool.dk, pool.dv), torch.float32, pool.device)
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", (n,), torch.int32, pool.device)
+    _check(lib().gla_state_write(pool.handle, n, _ptr(slot_idx), _ptr(S), _stream()))
+
+
+def gla_state_read(pool: StatePool, n=None, slot_idx=None, S=None) -> torch.Tensor:
+    """Float32 states of slots slot_idx (int32 [n]) or 0..n-1 (decoded from a
+    16-bit pool), as S [n,H,dk,dv]."""
+    if n is None:
+        n = pool.n_slots if slot_idx is None else slot_idx.shape[0]
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", (n,), torch.int32, pool.device)
+    if S is None:
+        S = torch.empty((n, pool.H, pool.dk, pool.dv), dtype=torch.float32, device=pool.device)
+    _need(S, "S", (n, pool.H, pool.dk, pool.dv), torch.float32, pool.device)
+    _check(lib().gla_state_read(pool.handle, n, _ptr(slot_idx), _ptr(S), _stream()))
+    return S
 
 
 def gla_recurrent_step(pool: StatePool, q, k, v, g, slot_idx=None, out_dtype=None, o=None):

@@ -18,10 +18,14 @@
 using namespace gla;
 
 struct gla_state {
-  float* data;
+  float* data;                 // float32 states (GLA_STATE_F32), else NULL
   int64_t n_slots;
   int32_t H, dk, dv;
   int device;
+  int32_t format;              // gla_state_fmt
+  int16_t* mant;               // GLA_STATE_Q16: mantissas [n_slots][H][dk][dv]
+  int32_t* expo;               // and exponents [n_slots][H][dv]
+  void* base;                  // the allocation
 };
 
 namespace {
@@ -354,6 +358,59 @@ hipError_t run_fwd(const gla_dims* dims, const FwdPlan& p, WalkArgs a, StateView
   return e;
 }
 
+
+// A pool of n_slots states in `format`, zero-filled in stream order (zero
+// mantissas and exponents read as zero states too).
+gla_status alloc_pool(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, int32_t format, void* stream,
+                      gla_state** out) {
+  if (!out) return fail(GLA_ERR_INVALID_ARGUMENT, "out must not be NULL");
+  *out = nullptr;
+  if (n_slots < 1) return fail(GLA_ERR_INVALID_ARGUMENT, "n_slots must be >= 1 (got %lld)", (long long)n_slots);
+  TRY(check_heads(H, dk, dv));
+  const bool q16 = format == GLA_STATE_Q16;
+  const size_t slot = q16 ? (size_t)H * dk * dv * sizeof(int16_t) : gla_state_slot_bytes(H, dk, dv);
+  if ((size_t)n_slots > ((size_t)1 << 46) / slot)
+    return fail(GLA_ERR_OUT_OF_MEMORY, "pool of %lld slots is too large", (long long)n_slots);
+  const size_t mant_bytes = (size_t)n_slots * slot;
+  const size_t expo_off = q16 ? align256(mant_bytes) : mant_bytes;
+  const size_t bytes = q16 ? expo_off + (size_t)n_slots * H * dv * sizeof(int32_t) : mant_bytes;
+  int dev = 0;
+  TRY(device_err(hipGetDevice(&dev), "hipGetDevice"));
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return fail(GLA_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  }
+  e = hipMemsetAsync(p, 0, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return device_err(e, "hipMemsetAsync");
+  }
+  gla_state* s = new gla_state{q16 ? nullptr : (float*)p, n_slots, H, dk, dv, dev, format,
+                               q16 ? (int16_t*)p : nullptr, q16 ? (int32_t*)((char*)p + expo_off) : nullptr, p};
+  *out = s;
+  return ok();
+}
+
+
+
+gla_status state_io(const gla_state* pool, int64_t n, const int32_t* slot_idx, float* S, int write, void* stream,
+                    const char* what) {
+  if (!pool) return fail(GLA_ERR_INVALID_ARGUMENT, "pool must not be NULL");
+  if (n < 0) return fail(GLA_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %lld)", (long long)n);
+  if (!slot_idx && n > pool->n_slots)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "n=%lld exceeds the pool's %lld slots", (long long)n,
+                (long long)pool->n_slots);
+  if (n * pool->H > ((int64_t)1 << 31) - 1) return fail(GLA_ERR_UNSUPPORTED, "n*H too large");
+  if (n == 0) return ok();
+  TRY(check_ptr(S, "S", false));
+  if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
+  StateIoArgs a{S, pool->data, Q16Pool{pool->mant, pool->expo}, slot_idx, n, pool->H, write};
+  return device_err(launch_state_io(a, (hipStream_t)stream), what);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -376,31 +433,34 @@ size_t gla_state_slot_bytes(int32_t H, int32_t dk, int32_t dv) {
   return (size_t)H * dk * dv * sizeof(float);
 }
 
+
 gla_status gla_state_alloc(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, void* stream, gla_state** out) {
-  if (!out) return fail(GLA_ERR_INVALID_ARGUMENT, "out must not be NULL");
-  *out = nullptr;
-  if (n_slots < 1) return fail(GLA_ERR_INVALID_ARGUMENT, "n_slots must be >= 1 (got %lld)", (long long)n_slots);
-  TRY(check_heads(H, dk, dv));
-  const size_t slot = gla_state_slot_bytes(H, dk, dv);
-  if ((size_t)n_slots > ((size_t)1 << 46) / slot)
-    return fail(GLA_ERR_OUT_OF_MEMORY, "pool of %lld slots is too large", (long long)n_slots);
-  const size_t bytes = (size_t)n_slots * slot;
-  int dev = 0;
-  TRY(device_err(hipGetDevice(&dev), "hipGetDevice"));
-  void* p = nullptr;
-  hipError_t e = hipMalloc(&p, bytes);
-  if (e != hipSuccess || !p) {
-    (void)hipGetLastError();
-    return fail(GLA_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
-  }
-  e = hipMemsetAsync(p, 0, bytes, (hipStream_t)stream);
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return device_err(e, "hipMemsetAsync");
-  }
-  gla_state* s = new gla_state{(float*)p, n_slots, H, dk, dv, dev};
-  *out = s;
+  return alloc_pool(n_slots, H, dk, dv, GLA_STATE_F32, stream, out);
+}
+
+gla_status gla_state_alloc_q16(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, void* stream, gla_state** out) {
+  return alloc_pool(n_slots, H, dk, dv, GLA_STATE_Q16, stream, out);
+}
+
+int32_t gla_state_format(const gla_state* pool) { return pool ? pool->format : -1; }
+
+gla_status gla_state_q16_ptrs(const gla_state* pool, int64_t slot, int16_t** mant, int32_t** expo) {
+  if (!pool || !mant || !expo) return fail(GLA_ERR_INVALID_ARGUMENT, "pool, mant and expo must not be NULL");
+  if (pool->format != GLA_STATE_Q16) return fail(GLA_ERR_INVALID_ARGUMENT, "the pool does not hold 16-bit states");
+  if (slot < 0 || slot >= pool->n_slots)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "slot %lld out of range [0, %lld)", (long long)slot, (long long)pool->n_slots);
+  *mant = pool->mant + slot * (int64_t)pool->H * pool->dk * pool->dv;
+  *expo = pool->expo + slot * (int64_t)pool->H * pool->dv;
   return ok();
+}
+
+
+gla_status gla_state_write(gla_state* pool, int64_t n, const int32_t* slot_idx, const float* S, void* stream) {
+  return state_io(pool, n, slot_idx, const_cast<float*>(S), 1, stream, "gla_state_write launch");
+}
+
+gla_status gla_state_read(const gla_state* pool, int64_t n, const int32_t* slot_idx, float* S, void* stream) {
+  return state_io(pool, n, slot_idx, S, 0, stream, "gla_state_read launch");
 }
 
 gla_status gla_state_free(gla_state* pool) {
@@ -409,14 +469,14 @@ gla_status gla_state_free(gla_state* pool) {
   (void)hipGetDevice(&cur);
   (void)hipSetDevice(pool->device);
   hipError_t e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipFree(pool->data);
+  if (e == hipSuccess) e = hipFree(pool->base);
   (void)hipSetDevice(cur);
   delete pool;
   return device_err(e, "gla_state_free");
 }
 
 float* gla_state_ptr(const gla_state* pool, int64_t slot) {
-  if (!pool || slot < 0 || slot >= pool->n_slots) return nullptr;
+  if (!pool || !pool->data || slot < 0 || slot >= pool->n_slots) return nullptr;
   return pool->data + slot * (int64_t)pool->H * pool->dk * pool->dv;
 }
 
@@ -506,6 +566,8 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
     return fail(GLA_ERR_INVALID_ARGUMENT, "cu_seqlens must be a non-NULL, 4-byte aligned device array");
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
   if (!pool) return fail(GLA_ERR_INVALID_ARGUMENT, "pool must not be NULL");
+  if (pool->format != GLA_STATE_F32)
+    return fail(GLA_ERR_UNSUPPORTED, "the packed prefill writes float32 pools only (encode states with gla_state_write)");
   if (pool->H != dims->H || pool->dk != dims->dk || pool->dv != dims->dv)
     return fail(GLA_ERR_INVALID_ARGUMENT, "pool holds H=%d dk=%d dv=%d, call has H=%d dk=%d dv=%d", pool->H,
                 pool->dk, pool->dv, dims->H, dims->dk, dims->dv);
@@ -562,6 +624,11 @@ gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv, int3
   if (!g) return fail(GLA_ERR_INVALID_ARGUMENT, "g must not be NULL");
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
   TRY(check_ptr(o, "o", false));
+  if (pool->format == GLA_STATE_Q16) {
+    StepQ16Args a{q, k, v, g, Q16Pool{pool->mant, pool->expo}, slot_idx, o, B, H};
+    return device_err(launch_step_q16(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream),
+                      "gla_recurrent_step launch");
+  }
   StepArgs a{q, k, v, g, pool->data, slot_idx, o, B, H};
   return device_err(launch_step(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream),
                     "gla_recurrent_step launch");

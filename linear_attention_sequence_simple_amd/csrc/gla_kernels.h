@@ -106,6 +106,26 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, hipStream_t st);
 
+// 16-bit decode state (gla_state16.hip): int16 mantissas [slot][H][DK][DV]
+// and one int32 exponent per state column [slot][H][DV].
+struct Q16Pool {
+  int16_t* mant; int32_t* expo;
+};
+struct StepQ16Args {
+  const void* q; const void* k; const void* v; const float* g;
+  Q16Pool pool; const int32_t* slot_idx; void* o;
+  int64_t B; int H;
+};
+hipError_t launch_step_q16(const StepQ16Args& a, int in_bf16, int out_bf16, hipStream_t st);
+// n float32 states S [n][H][DK][DV] into (write != 0) or out of pool slots
+// slot_idx[i] (or i): pool_f32 for a float32 pool, q16 (mant set) for a
+// 16-bit one.
+struct StateIoArgs {
+  float* S; float* pool_f32; Q16Pool q16; const int32_t* slot_idx;
+  int64_t n; int H; int write;
+};
+hipError_t launch_state_io(const StateIoArgs& a, hipStream_t st);
+
 // Backward finish: see gla_bwd.hip.
 struct BwdFinishArgs {
   const float* rq;                    // [B,T,H] q_t.dq_t

@@ -101,6 +101,19 @@ def test_state_pool_validation(L):
     assert L.gla_state_free(None) == 0
 
 
+def test_q16_pool_validation(L):
+    h = ctypes.c_void_p()
+    assert L.gla_state_alloc_q16(0, 16, 96, 192, None, ctypes.byref(h)) == 1
+    assert L.gla_state_alloc_q16(4, 16, 96, 128, None, ctypes.byref(h)) == 2
+    assert L.gla_state_alloc_q16(4, 16, 96, 192, None, None) == 1
+    assert L.gla_state_format(None) == -1
+    m, e = ctypes.c_void_p(), ctypes.c_void_p()
+    assert L.gla_state_q16_ptrs(None, 0, ctypes.byref(m), ctypes.byref(e)) == 1
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    assert L.gla_state_write(None, 1, None, p, None) == 1 and "pool" in L.gla_last_error().decode()
+    assert L.gla_state_read(None, 1, None, p, None) == 1
+
+
 def test_packed_prefill_validation(L):
     d = dims()
     p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first

@@ -1,0 +1,226 @@
+"""16-bit decode state on the GPU (gla_state_alloc_q16, gla_state_write and
+gla_state_read, gla_recurrent_step on a 16-bit pool) against the oracle's
+q16_encode, q16_decode and step_q16.
+
+Encoding float32 states is exact arithmetic on both sides (a power-of-two
+scaling and one rounding to an integer), so gla_state_write must give the
+oracle's mantissas and exponents bit for bit and gla_state_read its decoded
+values.  A step forms the updated state in fp32 (the oracle in fp64) before
+rounding it, so the stored results may differ at a rounding boundary: o must
+be within the float32 decode bound (1e-4 of rms), the stored state within
+one quantum of the oracle's (2^e of the coarser exponent), with equal
+exponents except in columns whose maximum lies within 1e-6 of an exponent
+threshold.  Every step is checked from the state the GPU stored, so nothing
+compounds from step to step.  Separately, 64 steps against the float64
+recurrence bound what the format costs (derived in the test).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import assert_close, assert_close_bf16_out, dev, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import linear_attention_sequence_simple_amd as gla
+    gla.lib()
+    return gla
+
+
+def _states(n, seed):
+    """N(0, 0.1^2) states with per-column scales 2^-30..2^30 (float32)."""
+    r = np.random.default_rng(seed)
+    S = r.standard_normal((n, 16, 96, 192)) * 0.1
+    S *= np.exp2(r.integers(-30, 31, size=(n, 16, 1, 192)))
+    return S.astype(np.float32)
+
+
+def _read_q16(pool, slots=None):
+    m, e = pool.q16_views()
+    if slots is not None:
+        idx = torch.as_tensor(np.asarray(slots, np.int64), device=dev())
+        m, e = m[idx], e[idx]
+    return m.cpu().numpy(), e.cpu().numpy()
+
+
+def _check_state(m, e, m_ref, e_ref, S_ref, name):
+    """Stored state against the oracle's: equal exponents except at a
+    threshold, every value within one quantum of the coarser exponent."""
+    M = np.abs(S_ref).max(axis=-2)
+    diff = e != e_ref
+    if diff.any():
+        r = M[diff] * np.exp2(-e_ref[diff].astype(np.float64))
+        dist = np.minimum.reduce([np.abs(r / t - 1) for t in (16383.75, 16384.0, 32767.5)])
+        assert np.all(dist < 1e-6), f"{name}: exponents differ away from a threshold"
+        assert np.all(np.abs(e[diff].astype(np.int64) - e_ref[diff]) == 1)
+    quantum = np.exp2(np.maximum(e, e_ref).astype(np.float64))[..., None, :]
+    gap = np.abs(oracle.q16_decode(m, e) - oracle.q16_decode(m_ref, e_ref))
+    assert np.all(gap <= quantum), f"{name}: {np.sum(gap > quantum)} values more than a quantum apart"
+    same_e = np.broadcast_to(~diff[..., None, :], m.shape)
+    moved = np.mean(m[same_e] != m_ref[same_e])
+    print(f"  {name}: {diff.sum()} exponents differ, {moved:.2e} of mantissas differ by 1", flush=True)
+
+
+def test_write_read_bitwise():
+    import linear_attention_sequence_simple_amd as gla
+    n, n_slots = 11, 20
+    S = _states(n, 1)
+    S[2, 3, :, 7] = 0.0
+    S[4, 0, 5, 9] = np.nan
+    S[4, 1, 6, 10] = np.inf
+    slots = np.random.default_rng(2).permutation(n_slots)[:n].astype(np.int32)
+    print("case q16 write/read", flush=True)
+    pool = gla.gla_state_alloc_q16(n_slots)
+    assert gla.gla_state_format(pool) == gla.GLA_STATE_Q16
+    sl = torch.from_numpy(slots).to(dev())
+    gla.gla_state_write(pool, torch.from_numpy(S).to(dev()), sl)
+    torch.cuda.synchronize()
+    m, e = _read_q16(pool)
+    m_ref, e_ref = oracle.q16_encode(S)
+    np.testing.assert_array_equal(m[slots], m_ref)
+    np.testing.assert_array_equal(e[slots], e_ref)
+    others = np.setdiff1d(np.arange(n_slots), slots)
+    assert not m[others].any() and not e[others].any()
+    back = gla.gla_state_read(pool, slot_idx=sl).cpu().numpy()
+    np.testing.assert_array_equal(back, oracle.q16_decode(m_ref, e_ref).astype(np.float32))
+    with pytest.raises(TypeError):
+        pool.view()
+    pool.free()
+
+
+def test_f32_pool_write_read():
+    import linear_attention_sequence_simple_amd as gla
+    pool = gla.gla_state_alloc(9)
+    assert gla.gla_state_format(pool) == gla.GLA_STATE_F32
+    S = _states(5, 3)
+    slots = torch.tensor([7, 0, 3, 8, 1], dtype=torch.int32, device=dev())
+    gla.gla_state_write(pool, torch.from_numpy(S).to(dev()), slots)
+    back = gla.gla_state_read(pool, slot_idx=slots)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(back.cpu().numpy(), S)
+    view = pool.view().cpu().numpy()
+    np.testing.assert_array_equal(view[[7, 0, 3, 8, 1]], S)
+    assert not view[[2, 4, 5, 6]].any()
+    pool.free()
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [(torch.bfloat16, torch.float32),
+                                                (torch.float32, torch.float32),
+                                                (torch.bfloat16, torch.bfloat16)])
+def test_steps_from_stored_state(in_dtype, out_dtype):
+    import linear_attention_sequence_simple_amd as gla
+    n, steps = 41, 6
+    print(f"case q16 steps in={in_dtype} out={out_dtype}", flush=True)
+    pool = gla.gla_state_alloc_q16(n)
+    gla.gla_state_write(pool, torch.from_numpy(gen.make_decode_state(n, seed=5)).to(dev()))
+    for step in range(steps):
+        m0, e0 = _read_q16(pool)
+        x = gen.make_decode_step(n, step, seed=5, dtype="bf16" if in_dtype == torch.bfloat16 else "f32")
+        o = gla.gla_recurrent_step(pool, to_dev(x["q"], in_dtype), to_dev(x["k"], in_dtype),
+                                   to_dev(x["v"], in_dtype), to_dev(x["g"], torch.float32), out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        o_ref, m_ref, e_ref = oracle.step_q16(m0, e0, x["q"], x["k"], x["v"], x["g"])
+        _, S_ref = oracle.step(oracle.q16_decode(m0, e0), x["q"], x["k"], x["v"], x["g"])
+        if out_dtype == torch.bfloat16:
+            assert_close_bf16_out(to_np(o), o_ref, TOL, f"o(bf16) step {step}")
+        else:
+            assert_close(to_np(o), o_ref, TOL, f"o step {step}")
+        m1, e1 = _read_q16(pool)
+        _check_state(m1, e1, m_ref, e_ref, S_ref, f"state step {step}")
+    pool.free()
+
+
+def test_slot_indices_special_decays_and_nan():
+    import linear_attention_sequence_simple_amd as gla
+    n_slots, B = 30, 9
+    print("case q16 slots/decays/nan", flush=True)
+    pool = gla.gla_state_alloc_q16(n_slots)
+    gla.gla_state_write(pool, torch.from_numpy(_states(n_slots, 6)).to(dev()))
+    slots = np.random.default_rng(7).permutation(n_slots)[:B].astype(np.int32)
+    x = gen.make_decode_step(B, 0, seed=7)
+    x["g"][0, :] = 0.0                       # gamma = 1
+    x["g"][1, :] = -np.inf                   # gamma = 0
+    x["v"][2, 3, 11] = np.nan                # one value channel of one head
+    m0, e0 = _read_q16(pool)
+    o = gla.gla_recurrent_step(pool, to_dev(x["q"], torch.bfloat16), to_dev(x["k"], torch.bfloat16),
+                               to_dev(x["v"], torch.bfloat16), to_dev(x["g"], torch.float32),
+                               slot_idx=torch.from_numpy(slots).to(dev()), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    m1, e1 = _read_q16(pool)
+    others = np.setdiff1d(np.arange(n_slots), slots)
+    np.testing.assert_array_equal(m1[others], m0[others])
+    np.testing.assert_array_equal(e1[others], e0[others])
+    o_ref, m_ref, e_ref = oracle.step_q16(m0[slots], e0[slots], x["q"], x["k"], x["v"], x["g"])
+    _, S_ref = oracle.step(oracle.q16_decode(m0[slots], e0[slots]), x["q"], x["k"], x["v"], x["g"])
+    # the NaN column: the NaN code throughout, exponent 0, o NaN there only
+    assert np.all(m1[slots[2], 3, :, 11] == oracle.Q16_NAN) and e1[slots[2], 3, 11] == 0
+    got = to_np(o)
+    assert np.isnan(got[2, 3, 11]) and np.isnan(o_ref[2, 3, 11])
+    keep = np.ones(got.shape, bool)
+    keep[2, 3, 11] = False
+    assert_close(got[keep], o_ref[keep], TOL, "o")
+    fin = np.ones(e_ref.shape, bool)
+    fin[2, 3, 11] = False
+    ms, es = m1[slots], e1[slots]
+    _check_state(np.where(fin[..., None, :], ms, 0), np.where(fin, es, 0), np.where(fin[..., None, :], m_ref, 0),
+                 np.where(fin, e_ref, 0), np.where(fin[..., None, :], S_ref, 0.0), "state")
+    pool.free()
+
+
+def test_packed_prefill_rejects_q16_pool():
+    import linear_attention_sequence_simple_amd as gla
+    pool = gla.gla_state_alloc_q16(4)
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device=dev())
+    cu = torch.tensor([0, 5, 9], dtype=torch.int32, device=dev())
+    with pytest.raises(gla.GlaError, match="UNSUPPORTED"):
+        gla.gla_chunk_fwd_varlen(z(9, 16, 96), z(9, 16, 96), z(9, 16, 192), z(9, 16, dt=torch.float32), cu, 5, pool)
+    pool.free()
+
+
+def test_decode_workload_sampled():
+    """1,280 sequences x 16 heads, the launch configuration the benchmark
+    times, 64 steps.  Each step of 16 sampled sequences against step_q16 from
+    the stored state; and o after 64 steps against the float64 recurrence.
+
+    The format's cost: each step rounds every stored value by at most half a
+    quantum, 2^-15 M with M the column maximum (M < 4.5 rms of a column of 96
+    near-Gaussian entries here), and the rounding of step j is then decayed
+    by the later gammas (mean 0.98).  The worst coherent sum is
+    2^-15 * 4.5 / (1 - 0.98) = 7e-3 of the state's rms; o, a 96-term sum with
+    random signs, carries the same relative error.  The bound is 1e-2."""
+    import linear_attention_sequence_simple_amd as gla
+    n, steps = 1280, 64
+    print("case q16 decode workload", flush=True)
+    S0 = gen.make_decode_state(n, seed=0)
+    pool = gla.gla_state_alloc_q16(n)
+    gla.gla_state_write(pool, torch.from_numpy(S0).to(dev()))
+    sample = np.arange(0, n, n // 16)
+    S64 = S0[sample].astype(np.float64)
+    worst = 0.0
+    for step in range(steps):
+        x = gen.make_decode_step(n, step, seed=0)
+        m0, e0 = _read_q16(pool, sample) if step % 16 == 0 else (None, None)
+        o = gla.gla_recurrent_step(pool, to_dev(x["q"], torch.bfloat16), to_dev(x["k"], torch.bfloat16),
+                                   to_dev(x["v"], torch.bfloat16), to_dev(x["g"], torch.float32),
+                                   out_dtype=torch.float32)
+        xs = {key: x[key][sample] for key in ("q", "k", "v", "g")}
+        o64, S64 = oracle.step(S64, xs["q"], xs["k"], xs["v"], xs["g"])
+        got = to_np(o)[sample]
+        rms = np.sqrt(np.mean(o64 * o64))
+        worst = max(worst, float(np.max(np.abs(got - o64)) / rms))
+        if m0 is not None:
+            o_ref, m_ref, e_ref = oracle.step_q16(m0, e0, xs["q"], xs["k"], xs["v"], xs["g"])
+            _, S_ref = oracle.step(oracle.q16_decode(m0, e0), xs["q"], xs["k"], xs["v"], xs["g"])
+            assert_close(got, o_ref, TOL, f"o step {step}")
+            m1, e1 = _read_q16(pool, sample)
+            _check_state(m1, e1, m_ref, e_ref, S_ref, f"state step {step}")
+    print(f"  o against the float64 recurrence over {steps} steps: max|err|/rms = {worst:.3e}", flush=True)
+    assert worst <= 1e-2
+    pool.free()
