@@ -31,6 +31,10 @@ def test_decode_bytes_from_shapes():
     state = n * H * DK * DV * 4 * 2     # read and written in place
     io = n * H * (2 * DK * 2 + DV * 2 + 4 + DV * 4)    # bf16 q, k, v; fp32 g; fp32 o
     assert bench.decode_bytes(n) == state + io
+    # 16-bit state: 96 x 192 int16 mantissas and 192 int32 exponents per
+    # (sequence, head), read and written: 2 x 37,632 B
+    assert bench.decode_bytes(n, q16=True) == n * H * (2 * 37_632) + io
+    assert bench.decode_bytes(1, q16=True) // H == 76_804
 
 
 def test_packed_bytes_match_the_workload():
