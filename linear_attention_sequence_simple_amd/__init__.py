@@ -388,6 +388,8 @@ class StatePool:
         return self._h
 
     def ptr(self, slot=0) -> int:
+        if self.fmt != GLA_STATE_F32:
+            raise TypeError("a 16-bit pool has no float32 slots: use q16_views() or gla_state_read")
         p = lib().gla_state_ptr(self.handle, slot)
         if not p:
             raise IndexError(f"slot {slot} out of range [0, {self.n_slots})")
