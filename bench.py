@@ -454,6 +454,15 @@ def bench_decode(torch, gla, layers=24, steps=64, warmup=1, parity=True, q16=Fal
         res["parity"] = {"o_last_step" + sfx: _rel_err(o_last, o_ref),
                          f"state_after_{steps}" + sfx: _rel_err(S_got, S_ref),
                          "layers_bitwise_equal": bool(same), "sample": f"{len(sample)} sequences x 16 heads"}
+        if q16:
+            # the kernel against the oracle from the same stored state: one more
+            # (untimed) step on layer 0, o of the sampled sequences
+            sl = torch.from_numpy(sample).to(dev)
+            m0, e0 = (t[sl].cpu().numpy() for t in pools[0].q16_views())
+            gla.gla_recurrent_step(pools[0], *xs[0], out_dtype=torch.float32, o=outs[0])
+            x = gen.make_decode_step(n, 0, seed=0)
+            o1_ref, _, _ = oracle.step_q16(m0, e0, x["q"][sample], x["k"][sample], x["v"][sample], x["g"][sample])
+            res["parity"]["o_one_step_from_stored_state"] = _rel_err(outs[0].cpu().numpy()[sample], o1_ref)
     for p in pools + [scratch]:
         p.free()
     return res
