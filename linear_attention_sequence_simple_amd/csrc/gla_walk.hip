@@ -582,26 +582,25 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
 
   TileRegs<bf16, DK, NTHR> px;                          // keys of the chunk being staged
   TileRegs<bf16, DVS, NTHR> py;                         // and its values
-  // an output wave's 32 query rows: 12 pieces of 16 bytes per row, 6 per lane
+  // an output wave's 32 query rows: lane l loads half of row l/2, 96
+  // contiguous bytes as 6 pieces of 16 at immediate offsets from one 32-bit
+  // lane offset, under one row check (per-piece offsets would be held as
+  // 64-bit values across the chunk loop and spilled)
   uint4 qr[OUTW ? 6 : 1];
+  const int qrow = lane >> 1, qcol = 48 * (lane & 1);
   auto load_q = [&](int n) {
     if constexpr (OUTW) {
       const int64_t t0 = (int64_t)n * CH + 32 * W;
-      const char* tile = tile_base(Qb, a.Q.st, t0, 32);
+      const char* p = tile_base(Qb, a.Q.st, t0, 32) + row_offset<bf16>(qrow, qcol, a.Q.st, 32);
+      const bool live = t0 + qrow < T;
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        const int p = lane + 64 * i, row = p / 12, cp = p % 12;
-        qr[i] = t0 + row < T ? *(const uint4*)(tile + row_offset<bf16>(row, cp * 8, a.Q.st, 32)) : make_uint4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < 6; ++i) qr[i] = live ? *(const uint4*)(p + 16 * i) : make_uint4(0, 0, 0, 0);
     }
   };
   auto stage_q = [&]() {
     if constexpr (OUTW) {
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        const int p = lane + 64 * i, row = p / 12, cp = p % 12;
-        *(uint4*)(sm.q + swz96(32 * W + row, cp * 8)) = qr[i];
-      }
+      for (int i = 0; i < 6; ++i) *(uint4*)(sm.q + swz96(32 * W + qrow, qcol + 8 * i)) = qr[i];
     }
   };
   // publish the state as a bf16 value/residual pair
