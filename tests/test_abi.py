@@ -3,6 +3,8 @@ point, and rejects bad arguments before any HIP call (no device needed)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -167,3 +169,18 @@ def test_backward_length_limit(L):
     d = dims(B=1, T=131_073, H=1)
     st = L.gla_chunk_bwd(ctypes.byref(d), p, p, p, p, None, p, None, p, p, p, p, None, p, 1 << 40, None)
     assert st == 2 and "1024 chunks" in L.gla_last_error().decode()
+
+
+def test_header_and_library_from_plain_c(tmp_path):
+    """include/gla.h compiles as C99 with every warning an error, and a C
+    program linked against libgla.so calls the host-side entry points."""
+    if shutil.which("gcc") is None or not os.path.exists(gla.lib_path()):
+        pytest.skip("gcc or libgla.so missing")
+    src = os.path.join(ROOT, "tests", "c", "abi_from_c.c")
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(gla.lib_path())
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", exe, "-L", libdir, "-lgla", "-Wl,-rpath," + libdir], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "FAIL" not in r.stdout
