@@ -132,7 +132,16 @@ FwdPlan plan_fwd(const gla_dims* d) {
                       : (out_bf16 ? WV_FWD_OUT_F32_BF16 : WV_FWD_OUT_F32_F32);
   p.ns = walk_slices(p.variant);
   p.n_chunks = (int)((d->T + CH - 1) / CH);
-  p.nseg = plan_segments(d->B * d->H * p.ns, p.n_chunks, "GLA_FWD_SEGMENTS");
+  const int64_t walkers = d->B * d->H * p.ns;
+  p.nseg = plan_segments(walkers, p.n_chunks, "GLA_FWD_SEGMENTS");
+  // fp32 walks: a chunk of the output walk costs about three of the
+  // state-only walk (31 against 10 us at B=1, T=2048), so once the launch is
+  // segmented anyway one chunk per segment shortens the chain most, as long
+  // as the output pass stays within four rounds of the chip (measured 161
+  // against 177 us for the default plan)
+  if (!in_bf16 && p.nseg > 1 && env_int("GLA_FWD_SEGMENTS", 0) <= 0 &&
+      walkers * p.n_chunks <= 4 * kTargetWorkgroups)
+    p.nseg = p.n_chunks;
   p.cps = (p.n_chunks + p.nseg - 1) / p.nseg;
   p.nseg = (p.n_chunks + p.cps - 1) / p.cps;
   const int64_t BH = d->B * d->H;
