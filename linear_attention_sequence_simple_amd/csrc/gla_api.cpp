@@ -289,7 +289,7 @@ BwdPlan plan_bwd(const gla_dims* d) {
   p.off_rq = off; off += tok;
   p.off_rk = off; off += tok;
   p.off_st = off; off += align256((size_t)BH * kStateElems * sizeof(float));
-  p.off_r = off; off += align256((size_t)BH * p.sp.n_chunks * sizeof(float));
+  p.off_r = off; off += align256((size_t)BH * (p.sp.n_chunks + 1) * sizeof(float));   // chunk totals, constants
   const size_t seg = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * kStateElems * sizeof(float)) : 0;
   const size_t dec = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * sizeof(float)) : 0;
   p.off_segf = off; off += seg;
