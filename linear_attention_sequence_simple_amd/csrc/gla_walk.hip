@@ -1022,12 +1022,31 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(float* buf, const float* 
   if (e >= DK * DV) return;
   const int64_t zrow = z0_idx ? (int64_t)z0_idx[bh / H] * H + bh % H : bh;
   f32x4 z = Z0 ? *(const f32x4*)(Z0 + zrow * DK * DV + e) : f32x4{0, 0, 0, 0};
-  for (int it = 0; it < nseg; ++it) {
-    const int s = rev ? nseg - 1 - it : it;
-    float* p = buf + (bh * nseg + s) * (int64_t)(DK * DV) + e;
-    const f32x4 d = *(const f32x4*)p;
-    *(f32x4*)p = z;
-    if (it + 1 < nseg) z = exp2f(decay[bh * nseg + s]) * z + d;
+  // Entries in groups of 8: the group's state changes and decays are all
+  // requested before its first store (each entry is read before it is
+  // overwritten), instead of one memory latency per entry.
+  constexpr int G = 8;
+  for (int it0 = 0; it0 < nseg; it0 += G) {
+    f32x4 d[G];
+    float dec[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int it = it0 + j;
+      if (it < nseg) {
+        const int s = rev ? nseg - 1 - it : it;
+        d[j] = *(const f32x4*)(buf + (bh * nseg + s) * (int64_t)(DK * DV) + e);
+        dec[j] = decay[bh * nseg + s];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int it = it0 + j;
+      if (it < nseg) {
+        const int s = rev ? nseg - 1 - it : it;
+        *(f32x4*)(buf + (bh * nseg + s) * (int64_t)(DK * DV) + e) = z;
+        if (it + 1 < nseg) z = exp2f(dec[j]) * z + d[j];
+      }
+    }
   }
 }
 
