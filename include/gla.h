@@ -34,6 +34,16 @@
  *    gla_last_error() in thread-local storage.  No exception crosses the ABI.
  *  - Outputs must not alias inputs.  Calls on different streams that share
  *    an output race.
+ *  - Contracts only the device can check (slot indices in range and
+ *    distinct, g <= 0 and not NaN, packed offsets in order, within the token
+ *    count and within max_seqlen) are checked when the environment sets
+ *    GLA_DEBUG to a non-empty value other than 0: the call then runs small
+ *    check kernels on `stream`, synchronises it, and returns
+ *    GLA_ERR_INVALID_ARGUMENT (naming the violation) before launching its own
+ *    kernels.  Such a call synchronises and allocates one word per device on
+ *    first use, so it cannot be captured in a graph; without GLA_DEBUG
+ *    nothing is checked on the device.  The convolution's history tensor is
+ *    the caller's, so only its negative and repeated slot indices are caught.
  */
 #ifndef GLA_H
 #define GLA_H
@@ -226,7 +236,7 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
  *   g    : [total_tokens, H] float32        o : [total_tokens, H, dv] out_dtype
  *   pool, slot_idx : sequence b uses slot slot_idx[b] (device int32 [B]) or
  *                 slot b when slot_idx is NULL; indices in range and
- *                 distinct (caller contract, not checked on the device).
+ *                 distinct (caller contract, checked on the device only under GLA_DEBUG).
  *   init_from_pool : 1 = start from the slot's state (a prompt continued),
  *                 0 = start from zero (a new prompt).
  *   The final state of every sequence is written to its slot.
@@ -254,7 +264,7 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens,
  *   q, k : [B, H, dk] in_dtype    v : [B, H, dv] in_dtype    g : [B, H] float32
  *   pool : states; sequence b uses slot slot_idx[b] (device int32 [B]) or
  *          slot b when slot_idx is NULL.  Indices must be in range and
- *          distinct (caller contract, not checked on the device).
+ *          distinct (caller contract, checked on the device only under GLA_DEBUG).
  *   o    : [B, H, dv] out_dtype.
  * A float32 pool is updated in float32.  A 16-bit pool (gla_state_alloc_q16)
  * is decoded, updated in float32 the same way, o is read from the updated

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgla.so")
 ARCH = "gfx950"
-SOURCES = ["gla_walk.hip", "gla_step.hip", "gla_state16.hip", "gla_bwd.hip", "gla_conv.hip", "gla_api.cpp"]
+SOURCES = ["gla_walk.hip", "gla_step.hip", "gla_state16.hip", "gla_bwd.hip", "gla_conv.hip", "gla_debug.hip",
+           "gla_api.cpp"]
 
 
 def hipcc() -> str:

@@ -10,9 +10,13 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "gla.h"
+#include "gla_debug.h"
 #include "gla_kernels.h"
 
 using namespace gla;
@@ -50,6 +54,53 @@ gla_status device_err(hipError_t e, const char* where) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- GLA_DEBUG: device-side checks of the caller contracts (gla_debug.hip)
+bool debug_on() {
+  const char* s = std::getenv("GLA_DEBUG");
+  return s && *s && std::strcmp(s, "0") != 0;
+}
+
+// One flag word per device, allocated on first use under GLA_DEBUG.
+int* debug_flag() {
+  static std::mutex mu;
+  static std::map<int, int*> flags;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = flags.find(dev);
+  if (it != flags.end()) return it->second;
+  int* p = nullptr;
+  if (hipMalloc(&p, sizeof(int)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  flags[dev] = p;
+  return p;
+}
+
+// Under GLA_DEBUG: clears the flag, runs checks(flag) (launches on st), reads
+// the flag back (synchronising st) and fails the call when a check found a
+// violation, before any of the call's own kernels is launched.
+template <class F>
+gla_status debug_checks(hipStream_t st, const char* call, F&& checks) {
+  if (!debug_on()) return GLA_OK;
+  int* flag = debug_flag();
+  if (!flag) return fail(GLA_ERR_OUT_OF_MEMORY, "%s: the GLA_DEBUG flag could not be allocated", call);
+  hipError_t e = debug_zero(flag, st);
+  if (e == hipSuccess) e = checks(flag);
+  int h = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, flag, sizeof h, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_err(e, "GLA_DEBUG checks");
+  if (!h) return GLA_OK;
+  std::string what;
+  if (h & DBG_SLOT_RANGE) what += " a slot index is out of range;";
+  if (h & DBG_SLOT_DUP) what += " a slot index is repeated;";
+  if (h & DBG_DECAY) what += " a log-decay is positive or NaN;";
+  if (h & DBG_OFFSETS) what += " sequence offsets are out of order or beyond their bounds;";
+  return fail(GLA_ERR_INVALID_ARGUMENT, "%s (GLA_DEBUG):%s", call, what.c_str());
+}
 
 gla_status check_ptr(const void* p, const char* name, bool nullable) {
   if (!p) return nullable ? GLA_OK : fail(GLA_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
@@ -415,6 +466,9 @@ gla_status state_io(const gla_state* pool, int64_t n, const int32_t* slot_idx, f
   if (n == 0) return ok();
   TRY(check_ptr(S, "S", false));
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
+  TRY(debug_checks((hipStream_t)stream, what, [&](int* f) {
+    return debug_slots(slot_idx, n, pool->n_slots, f, (hipStream_t)stream);
+  }));
   StateIoArgs a{S, pool->data, Q16Pool{pool->mant, pool->expo}, slot_idx, n, pool->H, write};
   return device_err(launch_state_io(a, (hipStream_t)stream), what);
 }
@@ -520,6 +574,9 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, con
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  TRY(debug_checks((hipStream_t)stream, "gla_chunk_fwd", [&](int* f) {
+    return debug_decay(g, dims->B, dims->T, dims->H, dims->T * dims->H, dims->H, 1, f, (hipStream_t)stream);
+  }));
   WalkArgs a = fwd_args(dims, p, q, k, v, g, o, dims->T);
   const int w = DV / p.ns;
   const hipError_t e = run_fwd(dims, p, a, state_plain(const_cast<float*>(S0), w), state_plain(S_T, w), ws,
@@ -548,6 +605,10 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q, const gla_
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  TRY(debug_checks((hipStream_t)stream, "gla_chunk_fwd_strided", [&](int* f) {
+    return sg ? debug_decay(g, dims->B, dims->T, dims->H, sg->batch, sg->token, sg->head, f, (hipStream_t)stream)
+              : debug_decay(g, dims->B, dims->T, dims->H, dims->T * dims->H, dims->H, 1, f, (hipStream_t)stream);
+  }));
   WalkArgs a = fwd_args(dims, p, q, k, v, g, o, dims->T);
   const int w = DV / p.ns;
   if (sq) a.Q = strided_view(q, *sq, 0);
@@ -594,6 +655,13 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  TRY(debug_checks((hipStream_t)stream, "gla_chunk_fwd_varlen", [&](int* f) {
+    hipStream_t s_ = (hipStream_t)stream;
+    hipError_t e_ = debug_offsets(cu_seqlens, dims->B, total_tokens, dims->T, f, s_);
+    if (e_ == hipSuccess) e_ = debug_slots(slot_idx, dims->B, pool->n_slots, f, s_);
+    if (e_ == hipSuccess && total_tokens > 0) e_ = debug_decay(g, 1, total_tokens, dims->H, 0, dims->H, 1, f, s_);
+    return e_;
+  }));
   // packed [total_tokens, H, cols] tensors: one "batch" row holding every token
   gla_dims packed = *dims;
   packed.B = 1;
@@ -633,6 +701,11 @@ gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv, int3
   if (!g) return fail(GLA_ERR_INVALID_ARGUMENT, "g must not be NULL");
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
   TRY(check_ptr(o, "o", false));
+  TRY(debug_checks((hipStream_t)stream, "gla_recurrent_step", [&](int* f) {
+    hipError_t e_ = debug_slots(slot_idx, B, pool->n_slots, f, (hipStream_t)stream);
+    if (e_ == hipSuccess) e_ = debug_decay(g, B, 1, H, H, 0, 1, f, (hipStream_t)stream);
+    return e_;
+  }));
   if (pool->format == GLA_STATE_Q16) {
     StepQ16Args a{q, k, v, g, Q16Pool{pool->mant, pool->expo}, slot_idx, o, B, H};
     return device_err(launch_step_q16(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream),
@@ -671,6 +744,13 @@ gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, in
   TRY(check_ptr(conv_state, "conv_state", true));
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
   TRY(check_ptr(y, "y", false));
+  // the history tensor is the caller's: its slot count is unknown here, so
+  // only negative and repeated indices are caught
+  TRY(debug_checks((hipStream_t)stream, "gla_conv1d_silu", [&](int* f) {
+    hipError_t e_ = cu_seqlens ? debug_offsets(cu_seqlens, B, total_tokens, T, f, (hipStream_t)stream) : hipSuccess;
+    if (e_ == hipSuccess && conv_state) e_ = debug_slots(slot_idx, B, INT64_MAX, f, (hipStream_t)stream);
+    return e_;
+  }));
   ConvArgs a{};
   a.x = x;
   a.w = w;
@@ -716,6 +796,9 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   const size_t osz = dims->out_dtype == GLA_BF16 ? 2 : 4;
   const int out_variant = dims->out_dtype == GLA_BF16 ? WV_FWD_OUT_BF16_BF16 : WV_FWD_OUT_BF16_F32;
   hipStream_t st = (hipStream_t)stream;
+  TRY(debug_checks(st, "gla_chunk_bwd", [&](int* f) {
+    return debug_decay(g, dims->B, dims->T, dims->H, dims->T * dims->H, dims->H, 1, f, st);
+  }));
   float* dq_part = (float*)(w + p.off_dq);
   float* dk_part = (float*)(w + p.off_dk);
   float* rq = (float*)(w + p.off_rq);

@@ -1,0 +1,137 @@
+"""GLA_DEBUG: the device-side checks of the caller contracts.
+
+With GLA_DEBUG=1 a call first checks on the device what the host cannot see
+(slot indices in range and distinct, log-decays not positive and not NaN,
+packed offsets in order and within bounds) and fails with
+GLA_ERR_INVALID_ARGUMENT before its kernels run; valid calls give the same
+results as without it.  Only violations that stay inside the tensors if a
+check missed them are run here: repeated slot indices, positive or NaN
+log-decays, offsets out of order (the kernels clamp those).  Out-of-range
+indices go through the same kernel and flag as repeated ones but are not run
+on the GPU: a missed one would reach the kernels' memory accesses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+from gpu_util import dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def gla():
+    import linear_attention_sequence_simple_amd as m
+    m.lib()
+    return m
+
+
+def _step_inputs(B, seed=1, H=16):
+    x = gen.make_decode_step(B, 0, H=H, seed=seed)
+    return [to_dev(x[k], torch.bfloat16) for k in ("q", "k", "v")] + [to_dev(x["g"], torch.float32)]
+
+
+def test_valid_calls_unchanged(gla, monkeypatch):
+    n = 6
+    S = torch.from_numpy(gen.make_decode_state(n, seed=2)).to(dev())
+    slots = torch.tensor([4, 0, 2], dtype=torch.int32, device=dev())
+    q, k, v, g = _step_inputs(3)
+    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=3, B=1, T=300, H=2)
+    fwd = lambda: gla.gla_chunk_fwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
+                                    to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32),
+                                    out_dtype=torch.float32)
+    out = {}
+    for mode in ("0", "1"):
+        print(f"case GLA_DEBUG={mode} valid calls", flush=True)
+        monkeypatch.setenv("GLA_DEBUG", mode)
+        pool = gla.gla_state_alloc(n)
+        gla.gla_state_write(pool, S)
+        o = gla.gla_recurrent_step(pool, q, k, v, g, slot_idx=slots, out_dtype=torch.float32)
+        of, Sf = fwd()
+        torch.cuda.synchronize()
+        out[mode] = (o.clone(), pool.view().clone(), of.clone(), Sf.clone())
+        pool.free()
+    for a, b in zip(out["0"], out["1"]):
+        assert torch.equal(a, b)
+
+
+def test_repeated_slots_rejected_before_any_kernel(gla, monkeypatch):
+    monkeypatch.setenv("GLA_DEBUG", "1")
+    print("case GLA_DEBUG repeated slots (step, state write, conv)", flush=True)
+    pool = gla.gla_state_alloc(8)
+    gla.gla_state_write(pool, torch.from_numpy(gen.make_decode_state(8, seed=4)).to(dev()))
+    before = pool.view().clone()
+    slots = torch.tensor([3, 5, 3], dtype=torch.int32, device=dev())
+    with pytest.raises(gla.GlaError, match="repeated"):
+        gla.gla_recurrent_step(pool, *_step_inputs(3), slot_idx=slots, out_dtype=torch.float32)
+    with pytest.raises(gla.GlaError, match="repeated"):
+        gla.gla_state_write(pool, torch.zeros((3, 16, 96, 192), device=dev()), slots)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.view(), before)          # no kernel touched the pool
+    hist = torch.zeros((4, 3, 64), dtype=torch.bfloat16, device=dev())
+    x = torch.ones((3, 10, 64), dtype=torch.bfloat16, device=dev())
+    w = torch.ones((64, 4), device=dev())
+    with pytest.raises(gla.GlaError, match="repeated"):
+        gla.gla_conv1d_silu(x, w, conv_state=hist, slot_idx=torch.tensor([1, 2, 1], dtype=torch.int32,
+                                                                          device=dev()), init_from_state=True)
+    torch.cuda.synchronize()
+    assert not hist.any()
+    pool.free()
+
+
+def test_bad_decay_rejected(gla, monkeypatch):
+    monkeypatch.setenv("GLA_DEBUG", "1")
+    print("case GLA_DEBUG positive and NaN log-decay (prefill, strided, backward, step)", flush=True)
+    d = gen.make_inputs("bwd_bf16_b4_t4096", seed=5, B=1, T=200, H=2, with_dO=True)
+    g = d["g"].copy()
+    g[0, 77, 1] = 0.25
+    q, k, v, dO = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v", "dO"))
+    with pytest.raises(gla.GlaError, match="positive or NaN"):
+        gla.gla_chunk_fwd(q, k, v, to_dev(g, torch.float32))
+    with pytest.raises(gla.GlaError, match="positive or NaN"):
+        gla.gla_chunk_fwd_strided(q, k, v, to_dev(g, torch.float32))
+    with pytest.raises(gla.GlaError, match="positive or NaN"):
+        gla.gla_chunk_bwd(q, k, v, to_dev(g, torch.float32), dO)
+    pool = gla.gla_state_alloc(2)
+    qs, ks, vs, gs = _step_inputs(2)
+    gs[1, 3] = float("nan")
+    with pytest.raises(gla.GlaError, match="positive or NaN"):
+        gla.gla_recurrent_step(pool, qs, ks, vs, gs)
+    # g = -inf (gamma = 0) is allowed
+    gs[1, 3] = float("-inf")
+    gla.gla_recurrent_step(pool, qs, ks, vs, gs)
+    torch.cuda.synchronize()
+    pool.free()
+
+
+def test_offsets_out_of_order_rejected(gla, monkeypatch):
+    monkeypatch.setenv("GLA_DEBUG", "1")
+    print("case GLA_DEBUG packed offsets out of order (prefill, conv)", flush=True)
+    d = gen.make_packed_inputs(seed=6, lengths=[50, 30, 40], n_slots=4, H=2)
+    pool = gla.gla_state_alloc(4, H=2)
+    cu = torch.tensor([0, 50, 30, 120], dtype=torch.int32, device=dev())
+    with pytest.raises(gla.GlaError, match="offsets"):
+        gla.gla_chunk_fwd_varlen(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
+                                 to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32), cu, 64, pool)
+    x = torch.ones((120, 64), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(gla.GlaError, match="offsets"):
+        gla.gla_conv1d_silu(x, torch.ones((64, 4), device=dev()), cu_seqlens=cu, max_seqlen=64)
+    # a length above max_seqlen is caught too
+    cu2 = torch.tensor([0, 50, 80, 120], dtype=torch.int32, device=dev())
+    with pytest.raises(gla.GlaError, match="offsets"):
+        gla.gla_chunk_fwd_varlen(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
+                                 to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32), cu2, 40, pool)
+    torch.cuda.synchronize()
+    pool.free()
+
+
+def test_no_checks_without_the_flag(gla, monkeypatch):
+    monkeypatch.delenv("GLA_DEBUG", raising=False)
+    print("case no GLA_DEBUG: a positive log-decay is the caller's contract, not checked", flush=True)
+    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=7, B=1, T=64, H=1)
+    g = d["g"].copy()
+    g[0, 3, 0] = 0.25
+    gla.gla_chunk_fwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
+                      to_dev(d["v"], torch.bfloat16), to_dev(g, torch.float32))
+    torch.cuda.synchronize()
