@@ -19,9 +19,15 @@ resident in HBM.  The same line carries, measured in the same run:
             B=8, T=2048, D=3,072, bf16 in/out, history kept per sequence
   fp32      prefill B=1, T=2048 with fp32 inputs and outputs
   roofline  the prefill walk kernel against the HBM roof (HIP events)
+  mfma_util the prefill's MFMA utilisation beside its ceiling (what the HBM
+            roof allows for its FLOPs and bytes) and a vendor-BLAS bf16 GEMM
+  prefill_mall_warm  the prefill right after kernels that wrote its inputs
+            (part may sit in the memory-side cache); labelled, not headline
   hbm_copy_reference  a plain device copy on rotating buffers: the streaming
             rate this GPU reaches, and each HBM-bound part as a fraction of it
   cpu_baseline  the fp64 oracle on the host cores, whole workload
+  cpu_baseline_decode  the oracle's decode step over one layer's 1,280 x 16
+            slots for 4 steps, extrapolated to 24 layers (labelled)
   parity    sampled max|err|/rms(ref) against the oracle for this run
 
 --only PART runs a single part a few times (for profiler counter passes):
@@ -53,9 +59,21 @@ H, DK, DV, CH = 16, 96, 192, 128
 
 # Algorithmic work per token-head (dense 128-token chunks):
 #   forward  = 2*C*dk + 2*C*dv + 2*dk*dv + 2*dk*dv = 147,456 flop
-#   backward = 2*C*(3dk + 2dv) + 3*2*dk*dv          = 282,624 flop
+#   backward = 2*C*(3dk + 2dv) + 3*2*dk*dv   chunk gradients
+#            + 2*dk*dv                        forward states recomputed
+#            + 2*dk*dv                        reverse state gradient
+#            = 356,352 flop
 FWD_FLOP_PER_TH = 2 * CH * DK + 2 * CH * DV + 4 * DK * DV
-BWD_FLOP_PER_TH = 2 * CH * (3 * DK + 2 * DV) + 6 * DK * DV
+BWD_FLOP_PER_TH = 2 * CH * (3 * DK + 2 * DV) + 10 * DK * DV
+
+
+def mfma_ceiling(flops, nbytes, peak_tflops, hbm_gbs=HBM_PEAK_GBS):
+    """The highest MFMA utilisation the roofline allows: the time the FLOPs
+    take at peak over the time the algorithmic bytes take at the HBM peak,
+    capped at 1 (a part whose bytes take longer can reach only that share)."""
+    t_flop = flops / (peak_tflops * 1e12)
+    t_byte = nbytes / (hbm_gbs * 1e9)
+    return 1.0 if t_byte <= t_flop else t_flop / t_byte
 
 
 def fwd_bytes(B, T, in_b, out_b, s0=False):
@@ -134,10 +152,68 @@ def cpu_baseline(max_pairs=128, seed=0, min_cpu_s=10.0, max_passes=6):
     T = gen.WORKLOADS["fwd_bf16_b8_t2048"]["T"]
     tokens = passes * len(pairs) / H * T * 1.0
     return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": (f"fp64 token-by-token oracle over {len(pairs)} of the {B * H} (b,h) "
                        f"sequences of the B={B} T={T} prefill workload, {passes} passes, one process "
                        f"per core (1 BLAS thread each); {sum(per):.1f} s of CPU work, {wall:.2f} s wall"),
             "cpu_seconds": sum(per)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_decode_chunk(args):
+    """`steps` oracle decode steps over `n` slots of one layer; returns the
+    CPU seconds of the steps alone (input generation is not timed)."""
+    chunk, n, steps = args
+    import oracle
+    S = gen.make_decode_state(n, seed=1000 + chunk)
+    spent = 0.0
+    for s in range(steps):
+        x = gen.make_decode_step(n, s, seed=1000 + chunk)
+        t0 = time.perf_counter()
+        _, S = oracle.step(S, x["q"], x["k"], x["v"], x["g"])
+        spent += time.perf_counter() - t0
+    return spent
+
+
+def cpu_decode_baseline(n_seq=1280, per_task=80, steps=4, layers=24, total_steps=64):
+    """The oracle's decode step over every slot of one layer (n_seq x 16 heads)
+    for `steps` steps, one process per core; the 24-layer, 64-step figure is a
+    linear extrapolation of that and is labelled as one.  The full fp64 state
+    of 24 layers (some 72 GB) is never held."""
+    import multiprocessing as mp
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    tasks = [(c, per_task, steps) for c in range(n_seq // per_task)]
+    os.environ["OMP_NUM_THREADS"] = "1"
+    with mp.get_context("fork").Pool(cores) as pool:
+        if threadpool_limits is not None:
+            with threadpool_limits(1):
+                per = pool.map(_oracle_decode_chunk, tasks, chunksize=1)
+        else:
+            per = pool.map(_oracle_decode_chunk, tasks, chunksize=1)
+    cpu_s = sum(per)
+    used = min(cores, len(tasks))
+    us_layer_step = cpu_s / used / steps * 1e6       # the steps' CPU time shared over the cores used
+    return {"us_per_layer_step": us_layer_step,
+            "tokens_per_s_24_layers": n_seq / (layers * us_layer_step * 1e-6),
+            "cores": used, "kind": "oracle", "extrapolated": True,
+            "sample": (f"fp64 oracle decode step over all {n_seq} x 16 slots of one layer for {steps} steps "
+                       f"({len(tasks)} tasks of {per_task} sequences, one process per core); per layer-step "
+                       f"time = {cpu_s:.1f} CPU s of the steps / {used} cores / {steps}; tokens/s for "
+                       f"{layers} layers x {total_steps} steps extrapolated linearly from it")}
 
 
 # --------------------------------------------------------------------------
@@ -224,7 +300,8 @@ def bench_prefill(torch, gla, steps, warmup, parity=True):
     flops = FWD_FLOP_PER_TH * B * T * H
     res = {"ms": ms, "tokens_per_s": tokens / (ms * 1e-3), "bytes": nbytes,
            "flops": flops, "GBps": nbytes / (ms * 1e-3) / 1e9,
-           "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "launches": 1 if ws_bytes == 0 else 3,
+           "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+           "mfma_ceiling": mfma_ceiling(flops, nbytes, BF16_PEAK_TFLOPS), "launches": 1 if ws_bytes == 0 else 3,
            "wall_s": wall}
     if parity:
         import oracle
@@ -237,6 +314,78 @@ def bench_prefill(torch, gla, steps, warmup, parity=True):
                          "S_T": _rel_err(S32.cpu().numpy()[np.ix_(bs, hs)], S_ref),
                          "sample": "(b,h) in {0,7}x{0,15}, all 2048 tokens"}
     return res
+
+
+def _per_launch_ms(torch, producer, fn, steps, warm_iters=20):
+    """Mean device time of fn() alone when each call follows producer():
+    events recorded between the two bracket fn's kernels only (the stream
+    runs in order, so the start event completes once the producer's kernels
+    have)."""
+    for _ in range(warm_iters):
+        producer()
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda._sleep(int(1e6))
+    for a, b in ev:
+        producer()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def bench_prefill_mall_warm(torch, gla, steps):
+    """The headline prefill with its inputs just written by a preceding
+    kernel, as the projection that produces q, k, v and the log-decay would
+    leave them: part of them may still sit in the memory-side (MALL) cache.
+    Beside it the same call after a producer that writes as many bytes to
+    other buffers, so both follow the same preceding work.  Reported apart
+    from the headline figure, which reads inputs that are resident in HBM."""
+    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=0)
+    B, T = d["meta"]["B"], d["meta"]["T"]
+    q, k, v, g, _, _ = _dev_inputs(torch, d, torch.bfloat16)
+    src = [x.clone() for x in (q, k, v, g)]
+    other = [torch.empty_like(x) for x in (q, k, v, g)]
+    o = torch.empty((B, T, H, DV), dtype=torch.bfloat16, device=q.device)
+    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=q.device)
+    fn = lambda: gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T)
+
+    def write_inputs():
+        for dst, x in zip((q, k, v, g), src):
+            dst.copy_(x)
+
+    def write_other():
+        for dst, x in zip(other, src):
+            dst.copy_(x)
+
+    warm = _per_launch_ms(torch, write_inputs, fn, steps)
+    cold = _per_launch_ms(torch, write_other, fn, steps)
+    nbytes = fwd_bytes(B, T, 2, 2)
+    in_bytes = sum(x.numel() * x.element_size() for x in src)
+    return {"label": "MALL-warm: inputs written by the kernels just before the call (not the headline figure)",
+            "ms_inputs_just_written": warm, "ms_after_other_writes": cold,
+            "tokens_per_s_inputs_just_written": B * T / (warm * 1e-3),
+            "tokens_per_s_after_other_writes": B * T / (cold * 1e-3),
+            "speedup": cold / warm, "input_bytes_written_before_each_call": in_bytes,
+            "GBps_algorithmic_inputs_just_written": nbytes / (warm * 1e-3) / 1e9,
+            "note": "events bracket each gla_chunk_fwd launch alone; the producer is four torch copies "
+                    "into the call's q, k, v, g (or, beside it, into other buffers of the same sizes)"}
+
+
+def mfma_reference(torch, steps=20):
+    """A large bf16 GEMM from the vendor BLAS (through torch.matmul): the dense
+    matrix rate this GPU reaches, a reference point beside the nominal peak."""
+    n = 8192
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    ms, _ = _time_calls(torch, lambda: torch.matmul(a, b, out=c), steps, 3, warm_ms=30)
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"TFLOPs": tf, "frac_of_nominal": tf / BF16_PEAK_TFLOPS,
+            "note": f"torch.matmul bf16 {n}x{n}x{n}, {steps} calls; a reference point, not a ceiling"}
 
 
 def bench_prefill_other(torch, gla, name, in_dtype, out_dtype, steps, warmup):
@@ -259,6 +408,7 @@ def bench_prefill_other(torch, gla, name, in_dtype, out_dtype, steps, warmup):
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "mfma_util": flops / (ms * 1e-3) / (peak * 1e12),
+            "mfma_ceiling": mfma_ceiling(flops, nbytes, peak),
             "mfma_peak": f"{'bf16' if ib == 2 else 'fp32'} {peak} TFLOP/s"}
 
 
@@ -482,6 +632,7 @@ def bench_backward(torch, gla, steps, warmup):
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "GBps_algorithmic": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+            "mfma_ceiling": mfma_ceiling(flops, nbytes, BF16_PEAK_TFLOPS),
             "kernels_per_call": "8: paired pass-1 state walks, 2 segment scans, dq/dv/dk walks, "
                                 "partial-sum finish, d-log-decay finish"}
 
@@ -565,6 +716,8 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline()       # before any GPU work
     print(f"[bench] cpu baseline done", file=sys.stderr, flush=True)
+    cpu_dec = None if args.no_cpu else cpu_decode_baseline()
+    print(f"[bench] cpu decode baseline done", file=sys.stderr, flush=True)
     torch, gla = _gpu()
     torch.cuda.synchronize()
     pre = bench_prefill(torch, gla, args.steps, args.warmup)
@@ -584,7 +737,11 @@ def main():
     fused = bench_fused(torch, gla, args.steps, args.warmup)
     print(f"[bench] fused {fused['ms']:.4f} ms", file=sys.stderr, flush=True)
     conv = bench_conv(torch, gla, max(3, args.steps // 2), 2)
+    mall = bench_prefill_mall_warm(torch, gla, args.steps)
+    print(f"[bench] prefill, inputs just written {mall['ms_inputs_just_written']:.4f} ms", file=sys.stderr,
+          flush=True)
     copy = copy_reference(torch, args.steps)
+    mref = mfma_reference(torch)
     print(f"[bench] conv {conv['ms']:.4f} ms", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -598,8 +755,12 @@ def main():
                      "kernel": "walk_kernel<bf16,bf16,3,0,false> (gla_chunk_fwd)",
                      "algorithmic_bytes_per_launch": pre["bytes"]},
         "mfma_util": {"value": pre["mfma_util"], "algorithmic_flop_per_step": pre["flops"],
-                      "peak": "bf16 dense 2500 TFLOP/s",
-                      "note": "dense 128-token chunks; the HBM roof caps this at ~0.40 for this workload"},
+                      "peak": "bf16 dense 2500 TFLOP/s", "ceiling": pre["mfma_ceiling"],
+                      "value_over_ceiling": pre["mfma_util"] / pre["mfma_ceiling"],
+                      "measured_gemm_reference": mref,
+                      "note": "dense 128-token chunks; ceiling = what the HBM roof allows for this "
+                              "workload's algorithmic bytes and FLOPs"},
+        "prefill_mall_warm": mall,
         "decode": dec, "decode_q16": dec16, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed, "fused": fused, "conv": conv,
         "parity": {"prefill": pre.get("parity")},
         "hbm_copy_reference": dict(copy, prefill_frac_of_copy=pre["GBps"] / copy["GBps"],
@@ -608,6 +769,7 @@ def main():
                                    decode_q16_frac_of_inplace=dec16["GBps"] / copy["inplace_GBps"],
                                    conv_frac_of_copy=conv["GBps"] / copy["GBps"]),
         "cpu_baseline": cpu,
+        "cpu_baseline_decode": cpu_dec,
         "kernel_source_digest": src_digest(),
     }
     print(json.dumps(out))

@@ -39,7 +39,8 @@ __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDi
            "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_write",
            "gla_state_read", "GLA_STATE_F32", "GLA_STATE_Q16",
-           "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS"]
+           "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS",
+           "chunk_fwd", "recurrent_step", "chunk_bwd"]
 
 GLA_F32, GLA_BF16 = 0, 1
 GLA_OP_FWD, GLA_OP_BWD = 0, 1
@@ -487,3 +488,16 @@ def gla_recurrent_step(pool: StatePool, q, k, v, g, slot_idx=None, out_dtype=Non
     _check(lib().gla_recurrent_step(B, H, DK, DV, in_code, out_code, _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(g), pool.handle, _ptr(slot_idx), _ptr(o), _stream()))
     return o
+
+
+# Short names: the three calls of the mixer without the C prefix.
+chunk_fwd = gla_chunk_fwd
+recurrent_step = gla_recurrent_step
+
+
+def chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, **kw):
+    """gla_chunk_bwd returning (dq, dk, dv, dg), followed by dS0 when an
+    initial state is given (or want_dS0=True is passed)."""
+    want = kw.pop("want_dS0", S0 is not None)
+    r = gla_chunk_bwd(q, k, v, g, dO, S0, dS_T, want_dS0=want, **kw)
+    return r if want else r[:4]
