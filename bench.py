@@ -25,6 +25,8 @@ resident in HBM.  The same line carries, measured in the same run:
             (part may sit in the memory-side cache); labelled, not headline
   hbm_copy_reference  a plain device copy on rotating buffers: the streaming
             rate this GPU reaches, and each HBM-bound part as a fraction of it
+  decode_after_prefix  the decode step on 1,280-slot pools whose states
+            came from 2,048- and from 8,192-token prefills: equal times
   cpu_baseline  the fp64 oracle on the host cores, whole workload
   cpu_baseline_decode  the oracle's decode step over one layer's 1,280 x 16
             slots for 4 steps, extrapolated to 24 layers (labelled)
@@ -374,6 +376,76 @@ def bench_prefill_mall_warm(torch, gla, steps):
                     "into the call's q, k, v, g (or, beside it, into other buffers of the same sizes)"}
 
 
+def bench_decode_after_prefix(torch, gla, steps=32, n=1280, group=160, piece=2048):
+    """Decode step time on pools whose states were built by prefills over
+    2,048 and over 8,192 tokens.  Each pool's n slots are filled `group`
+    sequences at a time by chained prefills of `piece` tokens (the final
+    state of one piece is the initial state of the next), the last writing
+    into the slots; every piece gets fresh inputs.  The state has the same
+    size whatever the prefix, so the two times must agree.  These prefill
+    inputs feed no parity check: they are drawn on the device from a seeded
+    torch generator (N(0,1)/sqrt(96) for q, k, v in bf16, logsigmoid(N(0,1) + 4)
+    for the log-decay)."""
+    dev = torch.device("cuda", 0)
+    gen_t = torch.Generator(device=dev)
+    gen_t.manual_seed(6)
+    rnd = lambda *shape: torch.randn(shape, generator=gen_t, device=dev)
+    sc = 1.0 / math.sqrt(DK)
+    q = torch.empty((group, piece, H, DK), dtype=torch.bfloat16, device=dev)
+    k, v = torch.empty_like(q), torch.empty((group, piece, H, DV), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((group, piece, H), dtype=torch.float32, device=dev)
+
+    def draw():
+        q.copy_(rnd(group, piece, H, DK) * sc)
+        k.copy_(rnd(group, piece, H, DK) * sc)
+        v.copy_(rnd(group, piece, H, DV) * sc)
+        g.copy_(torch.nn.functional.logsigmoid(rnd(group, piece, H) + 4.0))
+
+    o = torch.empty((group, piece, H, DV), dtype=torch.bfloat16, device=dev)
+    tmp = [torch.empty((group, H, DK, DV), dtype=torch.float32, device=dev) for _ in range(2)]
+    pools = {}
+    for prefix in (2048, 8192):
+        pool = gla.gla_state_alloc(n)
+        view = pool.view()
+        pieces = prefix // piece
+        for g0 in range(0, n, group):
+            S0 = None
+            for r in range(pieces):
+                draw()
+                dst = view[g0:g0 + group] if r == pieces - 1 else tmp[r % 2]
+                gla.gla_chunk_fwd(q, k, v, g, S0, out_dtype=torch.bfloat16, o=o, S_T=dst)
+                S0 = dst
+        pools[prefix] = pool
+    torch.cuda.synchronize()
+    a, b = pools[2048].view(), pools[8192].view()
+    res = {"state_rms_after_2048_tokens": float(a.pow(2).mean().sqrt()),
+           "state_rms_after_8192_tokens": float(b.pow(2).mean().sqrt()),
+           "states_max_abs_difference": float((a - b).abs().max())}
+    del q, k, v, g, o, tmp
+    xs = []
+    for st in range(8):
+        x = gen.make_decode_step(n, st, seed=2)
+        xs.append([torch.from_numpy(x[c]).to(dev).to(torch.bfloat16) for c in ("q", "k", "v")]
+                  + [torch.from_numpy(x["g"]).to(dev)])
+    out = torch.empty((n, H, DV), dtype=torch.float32, device=dev)
+    for prefix, pool in pools.items():
+        it = [0]
+
+        def fn():
+            x = xs[it[0] % len(xs)]
+            it[0] += 1
+            gla.gla_recurrent_step(pool, *x, out_dtype=torch.float32, o=out)
+
+        ms, _ = _time_calls(torch, fn, steps, 4, warm_ms=30)
+        res[f"us_per_step_after_{prefix}_tokens"] = ms * 1e3
+    for pool in pools.values():
+        pool.free()
+    res["ratio_8192_over_2048"] = res["us_per_step_after_8192_tokens"] / res["us_per_step_after_2048_tokens"]
+    res["note"] = (f"{n} sequences x 16 heads, one decode step per call, {steps} timed calls per pool; "
+                   "prefix states built by chained bf16 prefills of 2,048 tokens, fresh inputs per piece")
+    return res
+
+
 def mfma_reference(torch, steps=20):
     """A large bf16 GEMM from the vendor BLAS (through torch.matmul): the dense
     matrix rate this GPU reaches, a reference point beside the nominal peak."""
@@ -671,7 +743,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_q16", "backward", "packed", "conv", "fused",
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_q16", "backward", "packed", "conv", "fused", "prefix",
                                        "long", "copy"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -700,6 +772,8 @@ def main():
             print(json.dumps(bench_conv(torch, gla, args.steps, args.warmup)))
         elif args.only == "fused":
             print(json.dumps(bench_fused(torch, gla, args.steps, args.warmup)))
+        elif args.only == "prefix":
+            print(json.dumps(bench_decode_after_prefix(torch, gla)))
         elif args.only == "long":
             print(json.dumps(bench_prefill_other(torch, gla, "fwd_bf16_b1_t65536", torch.bfloat16, torch.bfloat16,
                                                  args.steps, args.warmup)))
@@ -737,6 +811,9 @@ def main():
     fused = bench_fused(torch, gla, args.steps, args.warmup)
     print(f"[bench] fused {fused['ms']:.4f} ms", file=sys.stderr, flush=True)
     conv = bench_conv(torch, gla, max(3, args.steps // 2), 2)
+    pfx = bench_decode_after_prefix(torch, gla)
+    print(f"[bench] decode after 2,048 / 8,192-token prefixes: {pfx['us_per_step_after_2048_tokens']:.1f} / "
+          f"{pfx['us_per_step_after_8192_tokens']:.1f} us", file=sys.stderr, flush=True)
     mall = bench_prefill_mall_warm(torch, gla, args.steps)
     print(f"[bench] prefill, inputs just written {mall['ms_inputs_just_written']:.4f} ms", file=sys.stderr,
           flush=True)
@@ -761,6 +838,7 @@ def main():
                       "note": "dense 128-token chunks; ceiling = what the HBM roof allows for this "
                               "workload's algorithmic bytes and FLOPs"},
         "prefill_mall_warm": mall,
+        "decode_after_prefix": pfx,
         "decode": dec, "decode_q16": dec16, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed, "fused": fused, "conv": conv,
         "parity": {"prefill": pre.get("parity")},
         "hbm_copy_reference": dict(copy, prefill_frac_of_copy=pre["GBps"] / copy["GBps"],
