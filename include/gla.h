@@ -41,8 +41,9 @@
  *    check kernels on `stream`, synchronises it, and returns
  *    GLA_ERR_INVALID_ARGUMENT (naming the violation) before launching its own
  *    kernels.  Such a call synchronises and allocates one word per device on
- *    first use, so it cannot be captured in a graph; without GLA_DEBUG
- *    nothing is checked on the device.  The convolution's history tensor is
+ *    first use, so it cannot be captured in a graph.  The checks of calls
+ *    from several host threads run one at a time (the flag word is shared);
+ *    without GLA_DEBUG nothing is checked on the device.  The convolution's history tensor is
  *    the caller's, so only its negative and repeated slot indices are caught.
  */
 #ifndef GLA_H

@@ -79,12 +79,20 @@ int* debug_flag() {
   return p;
 }
 
+// Held from clearing a device's flag to reading it back, so that calls from
+// several host threads under GLA_DEBUG never share a flag's contents.
+std::mutex& debug_mutex() {
+  static std::mutex mu;
+  return mu;
+}
+
 // Under GLA_DEBUG: clears the flag, runs checks(flag) (launches on st), reads
 // the flag back (synchronising st) and fails the call when a check found a
 // violation, before any of the call's own kernels is launched.
 template <class F>
 gla_status debug_checks(hipStream_t st, const char* call, F&& checks) {
   if (!debug_on()) return GLA_OK;
+  std::lock_guard<std::mutex> lock(debug_mutex());
   int* flag = debug_flag();
   if (!flag) return fail(GLA_ERR_OUT_OF_MEMORY, "%s: the GLA_DEBUG flag could not be allocated", call);
   hipError_t e = debug_zero(flag, st);

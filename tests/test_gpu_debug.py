@@ -135,3 +135,42 @@ def test_no_checks_without_the_flag(gla, monkeypatch):
     gla.gla_chunk_fwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
                       to_dev(d["v"], torch.bfloat16), to_dev(g, torch.float32))
     torch.cuda.synchronize()
+
+
+def test_threads_get_their_own_verdicts(gla, monkeypatch):
+    """Two host threads on their own streams under GLA_DEBUG: one makes valid
+    calls, the other calls with repeated slots.  Every valid call succeeds and
+    every invalid one fails, whatever the interleaving (the checks share one
+    flag word per device and run one call at a time)."""
+    import threading
+    monkeypatch.setenv("GLA_DEBUG", "1")
+    print("case GLA_DEBUG from two threads: valid and repeated slots", flush=True)
+    pool = gla.gla_state_alloc(8)
+    good = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev())
+    bad = torch.tensor([3, 3, 4], dtype=torch.int32, device=dev())
+    xs = _step_inputs(3)
+    torch.cuda.synchronize()
+    wrong = []
+
+    def run(slots, expect_ok):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for i in range(40):
+                try:
+                    gla.gla_recurrent_step(pool, *xs, slot_idx=slots, out_dtype=torch.float32)
+                    ok = True
+                except gla.GlaError:
+                    ok = False
+                if ok != expect_ok:
+                    wrong.append((expect_ok, i))
+        s.synchronize()
+
+    threads = [threading.Thread(target=run, args=(good, True)), threading.Thread(target=run, args=(bad, False))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not wrong, wrong
+    assert not pool.view()[3:].any()          # the invalid calls never reached the pool
+    pool.free()
