@@ -25,6 +25,8 @@ resident in HBM.  The same line carries, measured in the same run:
             (part may sit in the memory-side cache); labelled, not headline
   hbm_copy_reference  a plain device copy on rotating buffers: the streaming
             rate this GPU reaches, and each HBM-bound part as a fraction of it
+  device    the GPU's properties and the rates of a plain read, write and
+            fp32 GEMM it reaches (reference points)
   decode_after_prefix  the decode step on 1,280-slot pools whose states
             came from 2,048- and from 8,192-token prefills: equal times
   cpu_baseline  the fp64 oracle on the host cores, whole workload
@@ -362,8 +364,15 @@ def bench_prefill_mall_warm(torch, gla, steps):
         for dst, x in zip(other, src):
             dst.copy_(x)
 
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+
+    def write_flush():
+        flush.zero_()
+
     warm = _per_launch_ms(torch, write_inputs, fn, steps)
     cold = _per_launch_ms(torch, write_other, fn, steps)
+    flushed = _per_launch_ms(torch, write_flush, fn, steps)
+    del flush
     nbytes = fwd_bytes(B, T, 2, 2)
     in_bytes = sum(x.numel() * x.element_size() for x in src)
     return {"label": "MALL-warm: inputs written by the kernels just before the call (not the headline figure)",
@@ -371,9 +380,12 @@ def bench_prefill_mall_warm(torch, gla, steps):
             "tokens_per_s_inputs_just_written": B * T / (warm * 1e-3),
             "tokens_per_s_after_other_writes": B * T / (cold * 1e-3),
             "speedup": cold / warm, "input_bytes_written_before_each_call": in_bytes,
+            "ms_cold_after_512MB_flush": flushed,
+            "tokens_per_s_cold_after_512MB_flush": B * T / (flushed * 1e-3),
             "GBps_algorithmic_inputs_just_written": nbytes / (warm * 1e-3) / 1e9,
             "note": "events bracket each gla_chunk_fwd launch alone; the producer is four torch copies "
-                    "into the call's q, k, v, g (or, beside it, into other buffers of the same sizes)"}
+                    "into the call's q, k, v, g (or, beside it, into other buffers of the same sizes); "
+                    "the cold figure follows a 512 MB fill of another buffer, twice the memory-side cache"}
 
 
 def bench_decode_after_prefix(torch, gla, steps=32, n=1280, group=160, piece=2048):
@@ -444,6 +456,33 @@ def bench_decode_after_prefix(torch, gla, steps=32, n=1280, group=160, piece=204
     res["note"] = (f"{n} sequences x 16 heads, one decode step per call, {steps} timed calls per pool; "
                    "prefix states built by chained bf16 prefills of 2,048 tokens, fresh inputs per piece")
     return res
+
+
+def device_probe(torch, steps=20):
+    """What this GPU reports and reaches: its properties, and the rates of a
+    plain 1 GiB read (row sums), write (a fill) and an fp32 GEMM from the vendor
+    BLAS.  Reference points beside the nominal peaks, not ceilings."""
+    p = torch.cuda.get_device_properties(0)
+    n = 1 << 28                                          # 1 GiB of fp32
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    rows = x.view(n // 1024, 1024)
+    acc = torch.empty(n // 1024, dtype=torch.float32, device="cuda")
+    ms_r, _ = _time_calls(torch, lambda: torch.sum(rows, dim=1, out=acc), steps, 3, warm_ms=30)
+    ms_w, _ = _time_calls(torch, lambda: x.fill_(1.0), steps, 3, warm_ms=30)
+    del x, rows, acc
+    m = 8192
+    a = torch.randn((m, m), device="cuda")
+    b = torch.randn((m, m), device="cuda")
+    c = torch.empty((m, m), device="cuda")
+    ms_g, _ = _time_calls(torch, lambda: torch.matmul(a, b, out=c), max(3, steps // 4), 2, warm_ms=30)
+    del a, b, c
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "l2_bytes": getattr(p, "L2_cache_size", None),
+            "read_GBps": n * 4 / (ms_r * 1e-3) / 1e9, "write_GBps": n * 4 / (ms_w * 1e-3) / 1e9,
+            "fp32_gemm_TFLOPs": 2.0 * m ** 3 / (ms_g * 1e-3) / 1e12,
+            "note": "row sums of 1,024 floats over 1 GiB (read; 1 MB written), fill of 1 GiB (write), "
+                    "torch.matmul fp32 8192^3; torch's kernels, so lower bounds on what the chip "
+                    "reaches; reference points beside the nominal 8 TB/s and 157.3 TFLOP/s"}
 
 
 def mfma_reference(torch, steps=20):
@@ -743,7 +782,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_q16", "backward", "packed", "conv", "fused", "prefix",
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_q16", "backward", "packed", "conv", "fused", "prefix", "probe",
                                        "long", "copy"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -772,6 +811,8 @@ def main():
             print(json.dumps(bench_conv(torch, gla, args.steps, args.warmup)))
         elif args.only == "fused":
             print(json.dumps(bench_fused(torch, gla, args.steps, args.warmup)))
+        elif args.only == "probe":
+            print(json.dumps({"device": device_probe(torch), "mall": bench_prefill_mall_warm(torch, gla, args.steps)}))
         elif args.only == "prefix":
             print(json.dumps(bench_decode_after_prefix(torch, gla)))
         elif args.only == "long":
@@ -819,6 +860,7 @@ def main():
           flush=True)
     copy = copy_reference(torch, args.steps)
     mref = mfma_reference(torch)
+    probe = device_probe(torch)
     print(f"[bench] conv {conv['ms']:.4f} ms", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": pre["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -838,6 +880,7 @@ def main():
                       "note": "dense 128-token chunks; ceiling = what the HBM roof allows for this "
                               "workload's algorithmic bytes and FLOPs"},
         "prefill_mall_warm": mall,
+        "device": probe,
         "decode_after_prefix": pfx,
         "decode": dec, "decode_q16": dec16, "backward": bwd, "long_context": lc, "fp32": f32, "packed": packed, "fused": fused, "conv": conv,
         "parity": {"prefill": pre.get("parity")},
