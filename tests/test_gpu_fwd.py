@@ -115,6 +115,18 @@ def test_long_context_sampled_heads():
     assert np.isfinite(o).all()
 
 
+def test_one_head_262144_tokens():
+    """T = 262,144 on one head (2,048 chunks): the forward's largest segment
+    plan for a single head, 128 segments of 16 chunks with pass 1 in halves,
+    every output and the final state against the oracle."""
+    d = inputs("fwd_bf16_b1_t65536", seed=3, B=1, T=262_144, H=1)
+    print("case fwd one head T=262144", flush=True)
+    o, S = run_fwd(d, torch.bfloat16, torch.float32)
+    o_ref, S_ref = oracle.forward(d["q"], d["k"], d["v"], d["g"], d["S0"])
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "S_T")
+
+
 def test_deterministic_and_chaining():
     d = inputs("fwd_bf16_b8_t2048", seed=9, B=1, T=700, H=4, S0="normal0.1")
     o1, S1 = run_fwd(d, torch.bfloat16, torch.float32)
