@@ -127,6 +127,19 @@ def test_one_head_262144_tokens():
     assert_close(S, S_ref, TOL_BF16, "S_T")
 
 
+@pytest.mark.parametrize("B,T,H", [(512, 3, 16), (512, 129, 2)])
+def test_wide_batches(B, T, H):
+    """Many short sequences: B*H*2 walks (16,384 workgroups for B=512,
+    H=16), far more than the chip holds at once, every output and final state
+    against the oracle."""
+    d = inputs("fwd_bf16_b8_t2048", seed=4, B=B, T=T, H=H, S0="normal0.1")
+    print(f"case fwd wide batch B={B} T={T} H={H}", flush=True)
+    o, S = run_fwd(d, torch.bfloat16, torch.float32)
+    o_ref, S_ref = oracle.forward(d["q"], d["k"], d["v"], d["g"], d["S0"])
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "S_T")
+
+
 def test_deterministic_and_chaining():
     d = inputs("fwd_bf16_b8_t2048", seed=9, B=1, T=700, H=4, S0="normal0.1")
     o1, S1 = run_fwd(d, torch.bfloat16, torch.float32)
