@@ -61,6 +61,15 @@ def test_reduced(T, s0, dst):
     check(d, got, s0, dst)
 
 
+@pytest.mark.parametrize("B,T,H", [(128, 3, 16), (64, 130, 2)])
+def test_wide_batches(B, T, H):
+    """Many short sequences (2,048 (b, h) pairs for B=128, H=16): every
+    gradient against the oracle."""
+    d = inputs("bwd_bf16_b4_t4096", seed=5, B=B, T=T, H=H, S0="normal0.1", with_dO=True, with_dS_T=True)
+    print(f"case bwd wide batch B={B} T={T} H={H}", flush=True)
+    check(d, run_bwd(d))
+
+
 @pytest.mark.parametrize("g", ["one", "zero"])
 def test_special_decays(g):
     d = inputs("bwd_bf16_b4_t4096", seed=4, B=1, T=260, H=2, g=g, S0="normal0.1", with_dO=True,
