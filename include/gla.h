@@ -66,7 +66,7 @@ typedef enum {
 
 typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
 
-typedef enum { GLA_OP_FWD = 0, GLA_OP_BWD = 1 } gla_op;
+typedef enum { GLA_OP_FWD = 0, GLA_OP_BWD = 1, GLA_OP_FWD_VARLEN_Q16 = 2 } gla_op;
 
 /* Lower clamp of the log-decay inside the kernels; exp(-60) ~ 8.8e-27. */
 #define GLA_G_MIN (-60.0f)
@@ -163,7 +163,10 @@ gla_status gla_state_read(const gla_state* pool, int64_t n, const int32_t* slot_
                           float* S, void* stream);
 
 /* Workspace bytes that gla_chunk_fwd (op = GLA_OP_FWD) or gla_chunk_bwd
- * (op = GLA_OP_BWD) needs for `dims`.  Same validation as those calls. */
+ * (op = GLA_OP_BWD) needs for `dims`, or gla_chunk_fwd_varlen into a 16-bit
+ * pool (op = GLA_OP_FWD_VARLEN_Q16: the forward's bytes plus a float32 state
+ * per sequence and head, B x H x 73,728 bytes, where the final states are
+ * staged before encoding).  Same validation as those calls. */
 gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes);
 
 /* ---------------------------------------------------------------------------
@@ -240,12 +243,17 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
  *                 distinct (caller contract, checked on the device only under GLA_DEBUG).
  *   init_from_pool : 1 = start from the slot's state (a prompt continued),
  *                 0 = start from zero (a new prompt).
- *   The final state of every sequence is written to its slot.
- *   ws   : at least gla_workspace_size(GLA_OP_FWD, dims) bytes.
+ *   The final state of every sequence is written to its slot.  A 16-bit
+ *   pool (gla_state_alloc_q16) is read and written in its own format: the
+ *   slots' states are decoded into the workspace first (init_from_pool), the
+ *   walks run on float32 states there, and the final states are encoded into
+ *   the slots as gla_state_write does, so the slots hold exactly what
+ *   gla_state_write of the float32 result would give.
+ *   ws   : at least gla_workspace_size(GLA_OP_FWD, dims) bytes for a float32
+ *          pool, gla_workspace_size(GLA_OP_FWD_VARLEN_Q16, dims) for a
+ *          16-bit pool.
  * Errors: as gla_chunk_fwd, plus INVALID_ARGUMENT for a NULL or misaligned
- * cu_seqlens, a pool whose H/dk/dv differ, B > slots with slot_idx NULL;
- * UNSUPPORTED for a 16-bit pool (prefill into float32 states and encode them
- * with gla_state_write).
+ * cu_seqlens, a pool whose H/dk/dv differ, B > slots with slot_idx NULL.
  */
 gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens,
                                 const int32_t* cu_seqlens, const void* q,

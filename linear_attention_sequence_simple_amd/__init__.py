@@ -35,7 +35,7 @@ import os
 
 import torch
 
-__all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDims",
+__all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GLA_OP_FWD_VARLEN_Q16", "GlaError", "GlaDims",
            "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_write",
            "gla_state_read", "GLA_STATE_F32", "GLA_STATE_Q16",
@@ -43,7 +43,7 @@ __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GlaError", "GlaDi
            "chunk_fwd", "recurrent_step", "chunk_bwd"]
 
 GLA_F32, GLA_BF16 = 0, 1
-GLA_OP_FWD, GLA_OP_BWD = 0, 1
+GLA_OP_FWD, GLA_OP_BWD, GLA_OP_FWD_VARLEN_Q16 = 0, 1, 2
 GLA_STATE_F32, GLA_STATE_Q16 = 0, 1
 CHUNK, DK, DV = 128, 96, 192
 STATUS = {0: "GLA_OK", 1: "GLA_ERR_INVALID_ARGUMENT", 2: "GLA_ERR_UNSUPPORTED",
@@ -260,7 +260,8 @@ def gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool, slot_idx=None
     max_seqlen bounds every sequence's length; pool a StatePool; slot_idx
     int32 [n_seq] on the device or None (sequence b uses slot b).  Each
     sequence starts from its slot's state (init_from_pool) or from zero, and
-    its final state is written to the slot.  Returns o [N,H,192].
+    its final state is written to the slot (encoded, for a 16-bit pool).
+    Returns o [N,H,192].
     """
     N, H, _ = q.shape
     dev = q.device
@@ -280,7 +281,8 @@ def gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool, slot_idx=None
         o = torch.empty((N, H, DV), dtype=_torch_dtype(out_code), device=dev)
     _need(o, "o", (N, H, DV), _torch_dtype(out_code), dev)
     dims = _dims(n_seq, int(max_seqlen), H, in_code, out_code)
-    ws = _workspace(gla_workspace_size(GLA_OP_FWD, dims), dev, workspace)
+    op = GLA_OP_FWD_VARLEN_Q16 if pool.fmt == GLA_STATE_Q16 else GLA_OP_FWD
+    ws = _workspace(gla_workspace_size(op, dims), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gla_chunk_fwd_varlen(ctypes.byref(dims), N, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                       _ptr(g), pool.handle, _ptr(slot_idx), int(bool(init_from_pool)),

@@ -165,6 +165,10 @@ int plan_segments(int64_t walkers, int n_chunks, const char* env) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// float32 states of a packed prefill into a 16-bit pool, one per sequence and
+// head, staged in the workspace after the forward's own part
+size_t stage_bytes(const gla_dims* d) { return align256((size_t)d->B * d->H * kStateElems * sizeof(float)); }
+
 struct FwdPlan {
   int variant, ns, nseg, cps, n_chunks, fine;
   size_t ws_seg_states, ws_seg_decay, ws_total;
@@ -566,7 +570,11 @@ gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes) {
     *bytes = plan_bwd(dims).ws_total;
     return ok();
   }
-  return fail(GLA_ERR_INVALID_ARGUMENT, "op must be GLA_OP_FWD or GLA_OP_BWD (got %d)", op);
+  if (op == GLA_OP_FWD_VARLEN_Q16) {
+    *bytes = plan_fwd(dims).ws_total + stage_bytes(dims);
+    return ok();
+  }
+  return fail(GLA_ERR_INVALID_ARGUMENT, "op must be GLA_OP_FWD, GLA_OP_BWD or GLA_OP_FWD_VARLEN_Q16 (got %d)", op);
 }
 
 gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
@@ -644,8 +652,6 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
     return fail(GLA_ERR_INVALID_ARGUMENT, "cu_seqlens must be a non-NULL, 4-byte aligned device array");
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
   if (!pool) return fail(GLA_ERR_INVALID_ARGUMENT, "pool must not be NULL");
-  if (pool->format != GLA_STATE_F32)
-    return fail(GLA_ERR_UNSUPPORTED, "the packed prefill writes float32 pools only (encode states with gla_state_write)");
   if (pool->H != dims->H || pool->dk != dims->dk || pool->dv != dims->dv)
     return fail(GLA_ERR_INVALID_ARGUMENT, "pool holds H=%d dk=%d dv=%d, call has H=%d dk=%d dv=%d", pool->H,
                 pool->dk, pool->dv, dims->H, dims->dk, dims->dv);
@@ -661,8 +667,11 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
   TRY(check_ptr(g, "g", no_tokens));
   TRY(check_ptr(o, "o", no_tokens));
   const FwdPlan p = plan_fwd(dims);
-  if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
-  if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
+  const bool q16 = pool->format == GLA_STATE_Q16;
+  const size_t need = p.ws_total + (q16 ? stage_bytes(dims) : 0);
+  if (ws_bytes < need) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, need);
+  if (need > 0) TRY(check_ptr(ws, "ws", false));
+  if (q16 && dims->B * dims->H > ((int64_t)1 << 31) - 1) return fail(GLA_ERR_UNSUPPORTED, "B*H too large");
   TRY(debug_checks((hipStream_t)stream, "gla_chunk_fwd_varlen", [&](int* f) {
     hipStream_t s_ = (hipStream_t)stream;
     hipError_t e_ = debug_offsets(cu_seqlens, dims->B, total_tokens, dims->T, f, s_);
@@ -680,11 +689,25 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
   a.B = dims->B;
   a.cu = cu_seqlens;
   a.cu_total = total_tokens;
-  a.zinit_idx = a.zfin_idx = slot_idx;
   const int w = DV / p.ns;
-  const StateView zfin = state_plain(pool->data, w);
+  if (!q16) {
+    a.zinit_idx = a.zfin_idx = slot_idx;
+    const StateView zfin = state_plain(pool->data, w);
+    const StateView z0 = init_from_pool ? zfin : state_plain(nullptr, w);
+    const hipError_t e = run_fwd(dims, p, a, z0, zfin, ws, (hipStream_t)stream);
+    return device_err(e, "gla_chunk_fwd_varlen launch");
+  }
+  // 16-bit pool: sequence b's float32 state is row b of the staging area
+  float* stage = (float*)((char*)ws + p.ws_total);
+  const Q16Pool qp{pool->mant, pool->expo};
+  hipError_t e = hipSuccess;
+  if (init_from_pool) e = launch_state_io(StateIoArgs{stage, nullptr, qp, slot_idx, dims->B, dims->H, 0}, (hipStream_t)stream);
+  a.zinit_idx = a.zfin_idx = nullptr;
+  const StateView zfin = state_plain(stage, w);
   const StateView z0 = init_from_pool ? zfin : state_plain(nullptr, w);
-  const hipError_t e = run_fwd(dims, p, a, z0, zfin, ws, (hipStream_t)stream);
+  if (e == hipSuccess) e = run_fwd(dims, p, a, z0, zfin, ws, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = launch_state_io(StateIoArgs{stage, nullptr, qp, slot_idx, dims->B, dims->H, 1}, (hipStream_t)stream);
   return device_err(e, "gla_chunk_fwd_varlen launch");
 }
 

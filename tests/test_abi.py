@@ -62,6 +62,11 @@ def test_workspace_sizes(L):
     assert st == 2 and "bf16" in L.gla_last_error().decode()
     st, _ = ws_size(L, 7, dims())
     assert st == 1
+    # a packed prefill into a 16-bit pool stages one float32 state per
+    # sequence and head after the forward's own part
+    _, fwd = ws_size(L, gla.GLA_OP_FWD, dims())
+    st, q16 = ws_size(L, gla.GLA_OP_FWD_VARLEN_Q16, dims())
+    assert st == 0 and q16 - fwd == 2 * 16 * 96 * 192 * 4
 
 
 @pytest.mark.parametrize("kw,status", [

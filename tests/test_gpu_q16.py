@@ -174,14 +174,36 @@ def test_slot_indices_special_decays_and_nan():
     pool.free()
 
 
-def test_packed_prefill_rejects_q16_pool():
+@pytest.mark.parametrize("init", [False, True])
+def test_packed_prefill_into_q16_pool(init):
+    """The packed prefill into a 16-bit pool: o equals that of the same call
+    on a float32 pool bit for bit, and each used slot holds exactly what
+    gla_state_write of the float32 call's final state gives.  With
+    init_from_pool both calls start from the same decoded slot states; the
+    empty sequence's slot keeps its state."""
     import linear_attention_sequence_simple_amd as gla
-    pool = gla.gla_state_alloc_q16(4)
-    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device=dev())
-    cu = torch.tensor([0, 5, 9], dtype=torch.int32, device=dev())
-    with pytest.raises(gla.GlaError, match="UNSUPPORTED"):
-        gla.gla_chunk_fwd_varlen(z(9, 16, 96), z(9, 16, 96), z(9, 16, 192), z(9, 16, dt=torch.float32), cu, 5, pool)
-    pool.free()
+    n_slots = 6
+    d = gen.make_packed_inputs(seed=21, lengths=[300, 0, 129, 77], n_slots=n_slots)
+    q, k, v = (to_dev(d[c], torch.bfloat16) for c in ("q", "k", "v"))
+    g = to_dev(d["g"], torch.float32)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(dev())
+    used = torch.from_numpy(d["slot_idx"]).to(dev())
+    p16, p32 = gla.gla_state_alloc_q16(n_slots), gla.gla_state_alloc(n_slots)
+    if init:
+        gla.gla_state_write(p16, torch.from_numpy(_states(n_slots, 22)).to(dev()))
+        gla.gla_state_write(p32, gla.gla_state_read(p16))          # the decoded states
+    print(f"case packed prefill into a 16-bit pool, init={init}", flush=True)
+    o16 = gla.gla_chunk_fwd_varlen(q, k, v, g, cu, 300, p16, used, init_from_pool=init, out_dtype=torch.float32)
+    o32 = gla.gla_chunk_fwd_varlen(q, k, v, g, cu, 300, p32, used, init_from_pool=init, out_dtype=torch.float32)
+    ref = gla.gla_state_alloc_q16(n_slots)
+    gla.gla_state_write(ref, p32.view()[used.long()].contiguous(), used)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32)
+    m, e = _read_q16(p16, d["slot_idx"])
+    m_ref, e_ref = _read_q16(ref, d["slot_idx"])
+    assert np.array_equal(e, e_ref) and np.array_equal(m, m_ref)
+    for p in (p16, p32, ref):
+        p.free()
 
 
 def test_decode_workload_sampled():
