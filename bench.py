@@ -540,6 +540,16 @@ def bench_packed(torch, gla, steps, warmup):
     fn = lambda: gla.gla_chunk_fwd_varlen(q, k, v, g, cu, w["len_hi"], pool, slots, init_from_pool=False,
                                           out_dtype=torch.bfloat16, workspace=ws, o=o)
     ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
+    # the same call into a 16-bit pool (final states staged in float32, then encoded)
+    pool16 = gla.gla_state_alloc_q16(w["n_slots"])
+    ws16 = torch.empty(gla.gla_workspace_size(gla.GLA_OP_FWD_VARLEN_Q16, dims), dtype=torch.uint8, device=dev)
+    fn16 = lambda: gla.gla_chunk_fwd_varlen(q, k, v, g, cu, w["len_hi"], pool16, slots, init_from_pool=False,
+                                            out_dtype=torch.bfloat16, workspace=ws16, o=o)
+    ms16, _ = _time_calls(torch, fn16, steps, 2, warm_ms=30)
+    pool16.free()
+    del ws16
+    fn()                                   # o and the float32 slots of the call checked below
+    torch.cuda.synchronize()
     # sampled parity: the longest sequence, head 0, against the oracle (every
     # call starts from zero, so the slot holds that sequence's final state)
     import oracle
@@ -561,7 +571,8 @@ def bench_packed(torch, gla, steps, warmup):
                         f"({N} in all), H=16 bf16 in/out, final states into a {w['n_slots']}-slot pool",
             "ms": ms, "tokens_per_s": N / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "bytes": nbytes, "parity": parity}
+            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), "bytes": nbytes, "parity": parity,
+            "ms_into_16bit_pool": ms16, "tokens_per_s_into_16bit_pool": N / (ms16 * 1e-3)}
 
 
 def bench_fused(torch, gla, steps, warmup):
