@@ -154,7 +154,8 @@ gla_status gla_state_q16_ptrs(const gla_state* pool, int64_t slot, int16_t** man
  * pool, encoded as above for a 16-bit pool.  gla_state_read is the inverse
  * (exact for a 16-bit pool: every stored value is a float32).  Asynchronous
  * on `stream`; slot indices in range and distinct (caller contract).
- * This is how the float32 final states of a prefill enter a 16-bit pool.
+ * This is how the float32 final states of a prefill enter a 16-bit pool (the
+ * packed prefill, gla_chunk_fwd_varlen, does it by itself).
  * Errors: INVALID_ARGUMENT (NULL pool or S, n < 0, n > slots with slot_idx
  * NULL, misaligned slot_idx), UNSUPPORTED, DEVICE. */
 gla_status gla_state_write(gla_state* pool, int64_t n, const int32_t* slot_idx,
