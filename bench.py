@@ -288,16 +288,30 @@ def _rel_err(got, ref):
     return float(np.max(np.abs(got - ref)) / math.sqrt(float(np.mean(ref * ref))))
 
 
-def bench_prefill(torch, gla, steps, warmup, parity=True):
-    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=0)
+def bench_prefill(torch, gla, steps, warmup, parity=True, sets=3):
+    """The headline: one gla_chunk_fwd call per step on the training shape,
+    bf16 in and out.  The calls cycle over `sets` input/output sets (seeds
+    0..sets-1; 907 MB in all, more than the 256 MB memory-side cache), so
+    every call reads its inputs from HBM.  Parity reads the timed calls' own
+    bf16 o of set 0 on sampled (b, h) pairs, and also checks an fp32-output
+    call on the same inputs."""
+    ds = [gen.make_inputs("fwd_bf16_b8_t2048", seed=s) for s in range(sets)]
+    d = ds[0]
     B, T = d["meta"]["B"], d["meta"]["T"]
-    q, k, v, g, S0, _ = _dev_inputs(torch, d, torch.bfloat16)
-    o = torch.empty((B, T, H, DV), dtype=torch.bfloat16, device=q.device)
-    S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=q.device)
+    ins = [_dev_inputs(torch, x, torch.bfloat16)[:4] for x in ds]
+    dev = ins[0][0].device
+    outs = [(torch.empty((B, T, H, DV), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)) for _ in range(sets)]
     dims = gla.GlaDims(B, T, H, DK, DV, CH, gla.GLA_BF16, gla.GLA_BF16)
     ws_bytes = gla.gla_workspace_size(gla.GLA_OP_FWD, dims)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    fn = lambda: gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.bfloat16, o=o, S_T=S_T, workspace=ws)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def fn():
+        i = it[0] % sets
+        it[0] += 1
+        q, k, v, g = ins[i]
+        gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.bfloat16, o=outs[i][0], S_T=outs[i][1], workspace=ws)
     ms, wall = _time_calls(torch, fn, steps, warmup, warm_ms=100)
     tokens = B * T
     nbytes = fwd_bytes(B, T, 2, 2)
@@ -306,17 +320,23 @@ def bench_prefill(torch, gla, steps, warmup, parity=True):
            "flops": flops, "GBps": nbytes / (ms * 1e-3) / 1e9,
            "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
            "mfma_ceiling": mfma_ceiling(flops, nbytes, BF16_PEAK_TFLOPS), "launches": 1 if ws_bytes == 0 else 3,
-           "wall_s": wall}
+           "input_sets": sets, "wall_s": wall}
     if parity:
         import oracle
-        o32, S32 = gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.float32)
         torch.cuda.synchronize()
-        bs, hs = [0, 7], [0, 15]
+        q, k, v, g = ins[0]
+        o_timed = outs[0][0].float().cpu().numpy()
+        S_timed = outs[0][1].cpu().numpy()
+        o32, _ = gla.gla_chunk_fwd(q, k, v, g, None, out_dtype=torch.float32, want_state=False)
+        torch.cuda.synchronize()
+        bs, hs = [0, 4, 7], [0, 8, 15]
         sub = lambda x: x[np.ix_(bs, range(T), hs)]
         o_ref, S_ref = oracle.forward(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]), None)
-        res["parity"] = {"o_fp32_out": _rel_err(o32.cpu().numpy()[np.ix_(bs, range(T), hs)], o_ref),
-                         "S_T": _rel_err(S32.cpu().numpy()[np.ix_(bs, hs)], S_ref),
-                         "sample": "(b,h) in {0,7}x{0,15}, all 2048 tokens"}
+        res["parity"] = {"o_bf16_timed_call_over_bound": _bf16_out_ratio(sub(o_timed), o_ref, 1e-2),
+                         "S_T_timed_call": _rel_err(S_timed[np.ix_(bs, hs)], S_ref),
+                         "o_fp32_out": _rel_err(o32.cpu().numpy()[np.ix_(bs, range(T), hs)], o_ref),
+                         "sample": "(b,h) in {0,4,7}x{0,8,15}, all 2048 tokens, input set 0; bf16 o of the timed "
+                                   "calls against the elementwise bound 1e-2 rms + 2^-8 |ref| (at most 1 passes)"}
     return res
 
 

@@ -73,11 +73,21 @@ typedef enum { GLA_OP_FWD = 0, GLA_OP_BWD = 1, GLA_OP_FWD_VARLEN_Q16 = 2 } gla_o
 
 /* Problem sizes of a prefill or backward call.  B, T, H >= 1; T need not be
  * a multiple of `chunk` (the tail chunk is masked).  dk = 96, dv = 192,
- * chunk = 128.  in_dtype/out_dtype are gla_dtype values. */
+ * chunk = 128.  in_dtype/out_dtype are gla_dtype values.
+ *
+ * segments is the one plan choice a caller may make: 0 lets the library
+ * pick its launch plan (the default; a zero-initialised struct gets it);
+ * n > 0 splits every (batch, head) walk over the chunks into n segments of
+ * whole chunks (at most one per chunk), whose entering states come from a
+ * state-only pass and a scan over the segments.  Any plan computes the same
+ * recurrence; results differ only by rounding.  The workspace size depends
+ * on it, so pass the same dims to gla_workspace_size.  Negative values are
+ * INVALID_ARGUMENT. */
 typedef struct {
   int64_t B, T;
   int32_t H, dk, dv, chunk;
   int32_t in_dtype, out_dtype;
+  int32_t segments;
 } gla_dims;
 
 /* Opaque pool of per-sequence recurrent states. */

@@ -64,7 +64,7 @@ class GlaError(RuntimeError):
 class GlaDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("segments", ctypes.c_int32)]
 
 
 class GlaStrides(ctypes.Structure):
@@ -159,8 +159,10 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _dims(B, T, H, in_dtype, out_dtype) -> GlaDims:
-    return GlaDims(B, T, H, DK, DV, CHUNK, in_dtype, out_dtype)
+def _dims(B, T, H, in_dtype, out_dtype, segments=None) -> GlaDims:
+    """segments: None lets the library pick its launch plan; n > 0 splits every
+    walk into n segments of whole chunks (the dims' one plan choice)."""
+    return GlaDims(B, T, H, DK, DV, CHUNK, in_dtype, out_dtype, 0 if segments is None else int(segments))
 
 
 def gla_workspace_size(op: int, dims: GlaDims) -> int:
@@ -180,7 +182,7 @@ def _workspace(nbytes, device, workspace):
 
 
 def gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspace=None, o=None,
-                  S_T=None):
+                  S_T=None, segments=None):
     """Chunked prefill.  Returns (o, S_T); S_T is None when want_state is False."""
     B, T, H, _ = q.shape
     dev = q.device
@@ -199,7 +201,7 @@ def gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspac
         S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
     if S_T is not None:
         _need(S_T, "S_T", (B, H, DK, DV), torch.float32, dev)
-    dims = _dims(B, T, H, in_code, out_code)
+    dims = _dims(B, T, H, in_code, out_code, segments)
     ws = _workspace(gla_workspace_size(GLA_OP_FWD, dims), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gla_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
@@ -222,7 +224,7 @@ def _view_strides(t, name, shape, dtype, device):
 
 
 def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspace=None, o=None,
-                          S_T=None):
+                          S_T=None, segments=None):
     """gla_chunk_fwd on views with any positive batch/token/head strides (for
     example q, k, v sliced out of a fused projection output), rows contiguous."""
     B, T, H, _ = q.shape
@@ -242,7 +244,7 @@ def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, 
         S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
     if S_T is not None:
         _need(S_T, "S_T", (B, H, DK, DV), torch.float32, dev)
-    dims = _dims(B, T, H, in_code, out_code)
+    dims = _dims(B, T, H, in_code, out_code, segments)
     ws = _workspace(gla_workspace_size(GLA_OP_FWD, dims), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     r = ctypes.byref
@@ -252,7 +254,7 @@ def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, 
 
 
 def gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool, slot_idx=None,
-                         init_from_pool=False, out_dtype=None, workspace=None, o=None):
+                         init_from_pool=False, out_dtype=None, workspace=None, o=None, segments=None):
     """Prefill of packed sequences of different lengths into pool slots.
 
     q, k [N,H,96]; v [N,H,192]; g [N,H] float32; cu_seqlens int32 [n_seq+1]
@@ -280,7 +282,7 @@ def gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool, slot_idx=None
     if o is None:
         o = torch.empty((N, H, DV), dtype=_torch_dtype(out_code), device=dev)
     _need(o, "o", (N, H, DV), _torch_dtype(out_code), dev)
-    dims = _dims(n_seq, int(max_seqlen), H, in_code, out_code)
+    dims = _dims(n_seq, int(max_seqlen), H, in_code, out_code, segments)
     op = GLA_OP_FWD_VARLEN_Q16 if pool.fmt == GLA_STATE_Q16 else GLA_OP_FWD
     ws = _workspace(gla_workspace_size(op, dims), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -291,7 +293,7 @@ def gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool, slot_idx=None
 
 
 def gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None, want_dS0=False,
-                  workspace=None):
+                  workspace=None, segments=None):
     """Chunked backward.  Returns (dq, dk, dv, dg, dS0); dS0 is None unless want_dS0."""
     B, T, H, _ = q.shape
     dev = q.device
@@ -311,7 +313,7 @@ def gla_chunk_bwd(q, k, v, g, dO, S0=None, dS_T=None, out_dtype=None, want_dS0=F
     dv = torch.empty((B, T, H, DV), dtype=od, device=dev)
     dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_dS0 else None
-    dims = _dims(B, T, H, in_code, out_code)
+    dims = _dims(B, T, H, in_code, out_code, segments)
     ws = _workspace(gla_workspace_size(GLA_OP_BWD, dims), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gla_chunk_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),

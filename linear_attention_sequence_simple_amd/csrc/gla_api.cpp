@@ -141,25 +141,20 @@ gla_status check_dims(const gla_dims* d) {
     return fail(GLA_ERR_INVALID_ARGUMENT, "in_dtype/out_dtype must be GLA_F32 or GLA_BF16");
   if (d->B * d->H > (int64_t)1 << 24) return fail(GLA_ERR_UNSUPPORTED, "B*H too large");
   if ((d->T + CH - 1) / CH > (1 << 20)) return fail(GLA_ERR_UNSUPPORTED, "T too large");
+  if (d->segments < 0) return fail(GLA_ERR_INVALID_ARGUMENT, "segments must be >= 0 (got %d)", d->segments);
   return GLA_OK;
-}
-
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::atoi(s);
 }
 
 constexpr int64_t kStateElems = (int64_t)DK * DV;
 constexpr int kTargetWorkgroups = 256;   // one per compute unit
 
 // Segments per (batch, head, slice) walk: enough workgroups to cover the
-// chip, at least two chunks per segment.
-int plan_segments(int64_t walkers, int n_chunks, const char* env) {
+// chip, at least two chunks per segment; or the caller's count (dims->segments
+// > 0), at most one segment per chunk.
+int plan_segments(int64_t walkers, int n_chunks, int32_t forced) {
   int nseg = (int)std::max<int64_t>(1, (kTargetWorkgroups + walkers - 1) / walkers);
   nseg = std::min(nseg, std::max(1, n_chunks / 2));
-  const int forced = env_int(env, 0);
-  if (forced > 0) nseg = std::min(forced, n_chunks);
+  if (forced > 0) nseg = std::min<int>(forced, n_chunks);
   return std::max(1, nseg);
 }
 
@@ -196,13 +191,13 @@ FwdPlan plan_fwd(const gla_dims* d) {
   p.ns = walk_slices(p.variant);
   p.n_chunks = (int)((d->T + CH - 1) / CH);
   const int64_t walkers = d->B * d->H * p.ns;
-  p.nseg = plan_segments(walkers, p.n_chunks, "GLA_FWD_SEGMENTS");
+  p.nseg = plan_segments(walkers, p.n_chunks, d->segments);
   // fp32 walks: a chunk of the output walk costs about three of the
   // state-only walk (31 against 10 us at B=1, T=2048), so once the launch is
   // segmented anyway one chunk per segment shortens the chain most, as long
   // as the output pass stays within four rounds of the chip (measured 161
   // against 177 us for the default plan)
-  if (!in_bf16 && p.nseg > 1 && env_int("GLA_FWD_SEGMENTS", 0) <= 0 &&
+  if (!in_bf16 && p.nseg > 1 && d->segments <= 0 &&
       walkers * p.n_chunks <= 4 * kTargetWorkgroups)
     p.nseg = p.n_chunks;
   p.cps = (p.n_chunks + p.nseg - 1) / p.nseg;
@@ -340,7 +335,7 @@ BwdPlan plan_bwd(const gla_dims* d) {
   p.sp.n_chunks = (int)((d->T + CH - 1) / CH);
   p.sp.ns = DV / 96;
   const int64_t BH = d->B * d->H;
-  p.sp.nseg = plan_segments(BH * p.sp.ns, p.sp.n_chunks, "GLA_BWD_SEGMENTS");
+  p.sp.nseg = plan_segments(BH * p.sp.ns, p.sp.n_chunks, d->segments);
   p.sp.cps = (p.sp.n_chunks + p.sp.nseg - 1) / p.sp.nseg;
   p.sp.nseg = (p.sp.n_chunks + p.sp.cps - 1) / p.sp.cps;
   p.sp.fine = fine_factor(2 * BH * p.sp.ns * (p.sp.nseg - 1), p.sp.cps, true);   // two recurrences
@@ -671,7 +666,6 @@ gla_status gla_chunk_fwd_varlen(const gla_dims* dims, int64_t total_tokens, cons
   const size_t need = p.ws_total + (q16 ? stage_bytes(dims) : 0);
   if (ws_bytes < need) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, need);
   if (need > 0) TRY(check_ptr(ws, "ws", false));
-  if (q16 && dims->B * dims->H > ((int64_t)1 << 31) - 1) return fail(GLA_ERR_UNSUPPORTED, "B*H too large");
   TRY(debug_checks((hipStream_t)stream, "gla_chunk_fwd_varlen", [&](int* f) {
     hipStream_t s_ = (hipStream_t)stream;
     hipError_t e_ = debug_offsets(cu_seqlens, dims->B, total_tokens, dims->T, f, s_);

@@ -22,7 +22,7 @@ int main(void) {
   size_t bytes = 1;
   gla_state* pool = NULL;
   d.B = 8; d.T = 2048; d.H = 16; d.dk = 96; d.dv = 192; d.chunk = 128;
-  d.in_dtype = GLA_BF16; d.out_dtype = GLA_BF16;
+  d.in_dtype = GLA_BF16; d.out_dtype = GLA_BF16; d.segments = 0;
 
   CHECK(strcmp(gla_status_str(GLA_OK), "GLA_OK") == 0, "status string");
   CHECK(gla_workspace_size(GLA_OP_FWD, &d, &bytes) == GLA_OK && bytes == 0,
@@ -30,6 +30,12 @@ int main(void) {
   d.B = 1; d.T = 65536;
   CHECK(gla_workspace_size(GLA_OP_FWD, &d, &bytes) == GLA_OK && bytes > 0,
         "long context needs segment-state workspace");
+  d.segments = 4;
+  CHECK(gla_workspace_size(GLA_OP_FWD, &d, &bytes) == GLA_OK && bytes > 0,
+        "a caller's segment count needs segment-state workspace");
+  d.segments = -1;
+  CHECK(gla_workspace_size(GLA_OP_FWD, &d, &bytes) == GLA_ERR_INVALID_ARGUMENT, "negative segments are rejected");
+  d.segments = 0;
   d.dk = 64;
   CHECK(gla_workspace_size(GLA_OP_FWD, &d, &bytes) == GLA_ERR_UNSUPPORTED, "dk = 64 is unsupported");
   CHECK(strlen(gla_last_error()) > 0, "the failure leaves a message");

@@ -92,7 +92,7 @@ int main(int argc, char** argv) {
   /* prefill: bf16 in, fp32 out, S0 = 0 */
   gla_dims d;
   d.B = B; d.T = T; d.H = H; d.dk = 96; d.dv = 192; d.chunk = 128;
-  d.in_dtype = GLA_BF16; d.out_dtype = GLA_F32;
+  d.in_dtype = GLA_BF16; d.out_dtype = GLA_F32; d.segments = 0;
   void* q = to_device("q.bf16", tok * 96 * 2);
   void* k = to_device("k.bf16", tok * 96 * 2);
   void* v = to_device("v.bf16", tok * 192 * 2);

@@ -69,9 +69,27 @@ def test_workspace_sizes(L):
     assert st == 0 and q16 - fwd == 2 * 16 * 96 * 192 * 4
 
 
+def test_segments_plan_argument(L):
+    """dims.segments is the caller's plan choice: 0 keeps the library's plan,
+    n > 0 forces n segments (capped at one per chunk), and the workspace of
+    the segment states follows it.  No environment variable changes a plan."""
+    _, auto = ws_size(L, gla.GLA_OP_FWD, dims(B=8, T=2048, in_dtype=gla.GLA_BF16, out_dtype=gla.GLA_BF16))
+    assert auto == 0                                     # 256 walks fill the chip: one segment
+    st, forced = ws_size(L, gla.GLA_OP_FWD, dims(B=8, T=2048, segments=4))
+    assert st == 0 and forced >= 8 * 16 * 4 * 96 * 192 * 4 // 2
+    _, capped = ws_size(L, gla.GLA_OP_FWD, dims(B=1, T=300, segments=50))
+    _, three = ws_size(L, gla.GLA_OP_FWD, dims(B=1, T=300, segments=3))
+    assert capped == three                               # 3 chunks: at most 3 segments
+    _, b1 = ws_size(L, gla.GLA_OP_BWD, dims(B=8, T=2048, segments=1))
+    _, b4 = ws_size(L, gla.GLA_OP_BWD, dims(B=8, T=2048, segments=4))
+    assert b4 > b1
+    src = open(os.path.join(ROOT, "linear_attention_sequence_simple_amd", "csrc", "gla_api.cpp")).read()
+    assert re.findall(r'getenv\("([A-Z_]+)"\)', src) == ["GLA_DEBUG"]
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(T=0), 1), (dict(H=0), 1), (dict(dk=64), 2), (dict(dv=128), 2),
-    (dict(chunk=64), 2), (dict(in_dtype=5), 1), (dict(out_dtype=-1), 1)])
+    (dict(chunk=64), 2), (dict(in_dtype=5), 1), (dict(out_dtype=-1), 1), (dict(segments=-1), 1)])
 def test_dims_validation(L, kw, status):
     st, _ = ws_size(L, gla.GLA_OP_FWD, dims(**kw))
     assert st == status

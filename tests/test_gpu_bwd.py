@@ -15,23 +15,13 @@ TOL = 1e-2
 
 def run_bwd(d, S0=True, dS_T=True, out_dtype=torch.float32, segments=None):
     import linear_attention_sequence_simple_amd as gla
-    old = os.environ.get("GLA_BWD_SEGMENTS")
-    if segments is not None:
-        os.environ["GLA_BWD_SEGMENTS"] = str(segments)
-    try:
-        r = gla.gla_chunk_bwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
-                              to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32),
-                              to_dev(d["dO"], torch.bfloat16),
-                              S0=to_dev(d["S0"], torch.float32) if S0 else None,
-                              dS_T=to_dev(d.get("dS_T"), torch.float32) if dS_T else None,
-                              out_dtype=out_dtype, want_dS0=True)
-        torch.cuda.synchronize()
-    finally:
-        if segments is not None:
-            if old is None:
-                os.environ.pop("GLA_BWD_SEGMENTS")
-            else:
-                os.environ["GLA_BWD_SEGMENTS"] = old
+    r = gla.gla_chunk_bwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
+                          to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32),
+                          to_dev(d["dO"], torch.bfloat16),
+                          S0=to_dev(d["S0"], torch.float32) if S0 else None,
+                          dS_T=to_dev(d.get("dS_T"), torch.float32) if dS_T else None,
+                          out_dtype=out_dtype, want_dS0=True, segments=segments)
+    torch.cuda.synchronize()
     return [to_np(x) for x in r]
 
 

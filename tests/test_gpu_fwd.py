@@ -24,20 +24,10 @@ def _lib():
 
 def run_fwd(d, in_dtype, out_dtype, segments=None):
     import linear_attention_sequence_simple_amd as gla
-    old = os.environ.get("GLA_FWD_SEGMENTS")
-    if segments is not None:
-        os.environ["GLA_FWD_SEGMENTS"] = str(segments)
-    try:
-        o, S = gla.gla_chunk_fwd(to_dev(d["q"], in_dtype), to_dev(d["k"], in_dtype),
-                                 to_dev(d["v"], in_dtype), to_dev(d["g"], torch.float32),
-                                 to_dev(d["S0"], torch.float32), out_dtype=out_dtype)
-        torch.cuda.synchronize()
-    finally:
-        if segments is not None:
-            if old is None:
-                os.environ.pop("GLA_FWD_SEGMENTS")
-            else:
-                os.environ["GLA_FWD_SEGMENTS"] = old
+    o, S = gla.gla_chunk_fwd(to_dev(d["q"], in_dtype), to_dev(d["k"], in_dtype),
+                             to_dev(d["v"], in_dtype), to_dev(d["g"], torch.float32),
+                             to_dev(d["S0"], torch.float32), out_dtype=out_dtype, segments=segments)
+    torch.cuda.synchronize()
     return to_np(o), to_np(S)
 
 
@@ -100,6 +90,33 @@ def test_bf16_training_shape_sampled(g):
     assert_close(o[np.ix_(bs, range(2048), hs)], o_ref, TOL_BF16, "o")
     assert_close(S[np.ix_(bs, hs)], S_ref, TOL_BF16, "S_T")
     assert np.isfinite(o).all() and np.isfinite(S).all()
+
+
+@pytest.mark.parametrize("g", ["logsig_n4", "one", "zero"])
+def test_bf16_training_shape_bf16_out(g):
+    """The launch the benchmark times: B=8, H=16, T=2048, bf16 q, k, v in and
+    bf16 o out, S0 absent, S_T written, the library's default plan.  Sampled
+    (b, h) pairs (first, middle and last of each) over all 2,048 tokens
+    against the oracle, o elementwise within the bf16-output bound."""
+    import linear_attention_sequence_simple_amd as gla
+    d = inputs("fwd_bf16_b8_t2048", seed=0, g=g)
+    B, T = d["q"].shape[:2]
+    print(f"case fwd training shape bf16 out g={g}", flush=True)
+    q, k, v = (to_dev(d[c], torch.bfloat16) for c in ("q", "k", "v"))
+    gd = to_dev(d["g"], torch.float32)
+    o = torch.empty((B, T, 16, 192), dtype=torch.bfloat16, device=q.device)
+    S_T = torch.empty((B, 16, 96, 192), dtype=torch.float32, device=q.device)
+    dims = gla.GlaDims(B, T, 16, 96, 192, 128, gla.GLA_BF16, gla.GLA_BF16)
+    assert gla.gla_workspace_size(gla.GLA_OP_FWD, dims) == 0        # one walk launch, no segments
+    gla.gla_chunk_fwd(q, k, v, gd, None, out_dtype=torch.bfloat16, o=o, S_T=S_T)
+    torch.cuda.synchronize()
+    bs, hs = [0, 4, 7], [0, 8, 15]
+    sub = lambda x: x[np.ix_(bs, range(T), hs)]
+    o_ref, S_ref = oracle.forward(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]), None)
+    got = to_np(o)
+    assert_close_bf16_out(got[np.ix_(bs, range(T), hs)], o_ref, TOL_BF16, "o(bf16)")
+    assert_close(to_np(S_T)[np.ix_(bs, hs)], S_ref, TOL_BF16, "S_T")
+    assert np.isfinite(got).all()
 
 
 def test_long_context_sampled_heads():

@@ -32,9 +32,6 @@ def run_packed(d, in_dtype, out_dtype, init, max_seqlen=None, segments=None, n_s
     cu = d["cu_seqlens"] if cu is None else cu
     lengths = np.diff(cu)
     max_seqlen = int(max(1, lengths.max())) if max_seqlen is None else max_seqlen
-    old = os.environ.get("GLA_FWD_SEGMENTS")
-    if segments is not None:
-        os.environ["GLA_FWD_SEGMENTS"] = str(segments)
     try:
         N, H = d["q"].shape[:2]
         o = torch.full((N, H, 192), 7.0, dtype=out_dtype, device=dev())   # rows of no sequence keep 7
@@ -42,15 +39,10 @@ def run_packed(d, in_dtype, out_dtype, init, max_seqlen=None, segments=None, n_s
                                  to_dev(d["g"], torch.float32),
                                  torch.from_numpy(np.asarray(cu, np.int32)).to(dev()), max_seqlen, pool,
                                  torch.from_numpy(d["slot_idx"]).to(dev()), init_from_pool=init,
-                                 out_dtype=out_dtype, o=o)
+                                 out_dtype=out_dtype, o=o, segments=segments)
         torch.cuda.synchronize()
         out = to_np(o), to_np(pool.view())
     finally:
-        if segments is not None:
-            if old is None:
-                os.environ.pop("GLA_FWD_SEGMENTS")
-            else:
-                os.environ["GLA_FWD_SEGMENTS"] = old
         pool.free()
     return out
 
@@ -111,21 +103,11 @@ def test_packed_equals_batched(segments):
     d = gen.make_packed_inputs(seed=14, lengths=[T] * B, n_slots=B, H=H)
     d["slot_idx"] = np.arange(B, dtype=np.int32)
     o, pool = run_packed(d, torch.bfloat16, torch.bfloat16, True, segments=segments)
-    old = os.environ.get("GLA_FWD_SEGMENTS")
-    if segments is not None:
-        os.environ["GLA_FWD_SEGMENTS"] = str(segments)
-    try:
-        bt = lambda x, dt: to_dev(x.reshape((B, T) + x.shape[1:]), dt)
-        ob, Sb = gla.gla_chunk_fwd(bt(d["q"], torch.bfloat16), bt(d["k"], torch.bfloat16),
-                                   bt(d["v"], torch.bfloat16), bt(d["g"], torch.float32),
-                                   to_dev(d["pool"], torch.float32), out_dtype=torch.bfloat16)
-        torch.cuda.synchronize()
-    finally:
-        if segments is not None:
-            if old is None:
-                os.environ.pop("GLA_FWD_SEGMENTS")
-            else:
-                os.environ["GLA_FWD_SEGMENTS"] = old
+    bt = lambda x, dt: to_dev(x.reshape((B, T) + x.shape[1:]), dt)
+    ob, Sb = gla.gla_chunk_fwd(bt(d["q"], torch.bfloat16), bt(d["k"], torch.bfloat16),
+                               bt(d["v"], torch.bfloat16), bt(d["g"], torch.float32),
+                               to_dev(d["pool"], torch.float32), out_dtype=torch.bfloat16, segments=segments)
+    torch.cuda.synchronize()
     np.testing.assert_array_equal(o, to_np(ob).reshape(o.shape))
     np.testing.assert_array_equal(pool, to_np(Sb))
 

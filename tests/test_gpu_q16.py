@@ -174,16 +174,18 @@ def test_slot_indices_special_decays_and_nan():
     pool.free()
 
 
-@pytest.mark.parametrize("init", [False, True])
-def test_packed_prefill_into_q16_pool(init):
+@pytest.mark.parametrize("init,segments", [(False, None), (True, None), (False, 2), (True, 3), (True, 5)])
+def test_packed_prefill_into_q16_pool(init, segments):
     """The packed prefill into a 16-bit pool: o equals that of the same call
     on a float32 pool bit for bit, and each used slot holds exactly what
     gla_state_write of the float32 call's final state gives.  With
     init_from_pool both calls start from the same decoded slot states; the
-    empty sequence's slot keeps its state."""
+    empty sequence's slot keeps its state.  With several segments the
+    segment pass reads the staged float32 states as its initial states and
+    the walks write the final states back into the same staging rows."""
     import linear_attention_sequence_simple_amd as gla
     n_slots = 6
-    d = gen.make_packed_inputs(seed=21, lengths=[300, 0, 129, 77], n_slots=n_slots)
+    d = gen.make_packed_inputs(seed=21, lengths=[700, 0, 129, 77], n_slots=n_slots)
     q, k, v = (to_dev(d[c], torch.bfloat16) for c in ("q", "k", "v"))
     g = to_dev(d["g"], torch.float32)
     cu = torch.from_numpy(d["cu_seqlens"]).to(dev())
@@ -192,9 +194,11 @@ def test_packed_prefill_into_q16_pool(init):
     if init:
         gla.gla_state_write(p16, torch.from_numpy(_states(n_slots, 22)).to(dev()))
         gla.gla_state_write(p32, gla.gla_state_read(p16))          # the decoded states
-    print(f"case packed prefill into a 16-bit pool, init={init}", flush=True)
-    o16 = gla.gla_chunk_fwd_varlen(q, k, v, g, cu, 300, p16, used, init_from_pool=init, out_dtype=torch.float32)
-    o32 = gla.gla_chunk_fwd_varlen(q, k, v, g, cu, 300, p32, used, init_from_pool=init, out_dtype=torch.float32)
+    print(f"case packed prefill into a 16-bit pool, init={init} segments={segments}", flush=True)
+    o16 = gla.gla_chunk_fwd_varlen(q, k, v, g, cu, 700, p16, used, init_from_pool=init, out_dtype=torch.float32,
+                                   segments=segments)
+    o32 = gla.gla_chunk_fwd_varlen(q, k, v, g, cu, 700, p32, used, init_from_pool=init, out_dtype=torch.float32,
+                                   segments=segments)
     ref = gla.gla_state_alloc_q16(n_slots)
     gla.gla_state_write(ref, p32.view()[used.long()].contiguous(), used)
     torch.cuda.synchronize()

@@ -44,20 +44,6 @@ def fused_views(q, k, v, layout):
     return buf, qv, kv, vv
 
 
-def with_segments(n, fn):
-    old = os.environ.get("GLA_FWD_SEGMENTS")
-    if n is not None:
-        os.environ["GLA_FWD_SEGMENTS"] = str(n)
-    try:
-        return fn()
-    finally:
-        if n is not None:
-            if old is None:
-                os.environ.pop("GLA_FWD_SEGMENTS")
-            else:
-                os.environ["GLA_FWD_SEGMENTS"] = old
-
-
 @pytest.mark.parametrize("layout", ["blocked", "per_head"])
 @pytest.mark.parametrize("dtype,segments", [("bf16", None), ("bf16", 3), ("f32", None), ("f32", 3)])
 def test_fused_layout(layout, dtype, segments):
@@ -76,9 +62,8 @@ def test_fused_layout(layout, dtype, segments):
     gv.copy_(g)
     obuf = torch.full((B, T, H * DV + 64), 7.0, dtype=torch.float32, device=dev())
     ov = obuf[..., 32:32 + H * DV].unflatten(-1, (H, DV))
-    o_s, S_s = with_segments(segments, lambda: gla.gla_chunk_fwd_strided(qv, kv, vv, gv, S0, out_dtype=torch.float32,
-                                                                         o=ov))
-    o_d, S_d = with_segments(segments, lambda: gla.gla_chunk_fwd(q, k, v, g, S0, out_dtype=torch.float32))
+    o_s, S_s = gla.gla_chunk_fwd_strided(qv, kv, vv, gv, S0, out_dtype=torch.float32, o=ov, segments=segments)
+    o_d, S_d = gla.gla_chunk_fwd(q, k, v, g, S0, out_dtype=torch.float32, segments=segments)
     torch.cuda.synchronize()
     assert torch.equal(o_s, o_d) and torch.equal(S_s, S_d)
     assert torch.all(obuf[..., :32] == 7.0) and torch.all(obuf[..., 32 + H * DV:] == 7.0)

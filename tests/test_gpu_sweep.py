@@ -29,25 +29,6 @@ def _lib():
     return gla
 
 
-class _Env:
-    """Set an environment variable for the duration of a call."""
-
-    def __init__(self, name, value):
-        self.name, self.value = name, value
-
-    def __enter__(self):
-        self.old = os.environ.get(self.name)
-        if self.value is not None:
-            os.environ[self.name] = str(self.value)
-
-    def __exit__(self, *exc):
-        if self.value is not None:
-            if self.old is None:
-                os.environ.pop(self.name)
-            else:
-                os.environ[self.name] = self.old
-
-
 def _check_out(got, ref, in_dt, out_dt, name):
     tol = 1e-2 if in_dt == "bf16" else 1e-4
     if out_dt == "bf16":
@@ -77,11 +58,10 @@ def test_prefill_sweep(c):
     print(f"case prefill {c}", flush=True)
     wl = "fwd_bf16_b8_t2048" if c["in_dt"] == "bf16" else "fwd_f32_b1_t2048"
     d = gen.make_inputs(wl, seed=100 + c["i"], B=c["B"], T=c["T"], H=c["H"], S0=c["S0"], g=c["g"])
-    with _Env("GLA_FWD_SEGMENTS", c["seg"]):
-        o, S = gla.gla_chunk_fwd(to_dev(d["q"], TDT[c["in_dt"]]), to_dev(d["k"], TDT[c["in_dt"]]),
-                                 to_dev(d["v"], TDT[c["in_dt"]]), to_dev(d["g"], torch.float32),
-                                 to_dev(d["S0"], torch.float32), out_dtype=TDT[c["out_dt"]])
-        torch.cuda.synchronize()
+    o, S = gla.gla_chunk_fwd(to_dev(d["q"], TDT[c["in_dt"]]), to_dev(d["k"], TDT[c["in_dt"]]),
+                             to_dev(d["v"], TDT[c["in_dt"]]), to_dev(d["g"], torch.float32),
+                             to_dev(d["S0"], torch.float32), out_dtype=TDT[c["out_dt"]], segments=c["seg"])
+    torch.cuda.synchronize()
     o_ref, S_ref = oracle.forward(d["q"], d["k"], d["v"], d["g"], d["S0"])
     _check_out(to_np(o), o_ref, c["in_dt"], c["out_dt"], "o")
     assert_close(to_np(S), S_ref, 1e-2 if c["in_dt"] == "bf16" else 1e-4, "S_T")
@@ -108,12 +88,12 @@ def test_backward_sweep(c):
                         with_dO=True, with_dS_T=True)
     S0 = d["S0"] if c["S0"] else None
     dS_T = d["dS_T"] if c["dS_T"] else None
-    with _Env("GLA_BWD_SEGMENTS", c["seg"]):
-        got = gla.gla_chunk_bwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
-                                to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32),
-                                to_dev(d["dO"], torch.bfloat16), S0=to_dev(S0, torch.float32),
-                                dS_T=to_dev(dS_T, torch.float32), out_dtype=TDT[c["out_dt"]], want_dS0=True)
-        torch.cuda.synchronize()
+    got = gla.gla_chunk_bwd(to_dev(d["q"], torch.bfloat16), to_dev(d["k"], torch.bfloat16),
+                            to_dev(d["v"], torch.bfloat16), to_dev(d["g"], torch.float32),
+                            to_dev(d["dO"], torch.bfloat16), S0=to_dev(S0, torch.float32),
+                            dS_T=to_dev(dS_T, torch.float32), out_dtype=TDT[c["out_dt"]], want_dS0=True,
+                            segments=c["seg"])
+    torch.cuda.synchronize()
     ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], S0, dS_T)
     for name, x, y in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
         _check_out(to_np(x), y, "bf16", c["out_dt"], name)
@@ -145,13 +125,12 @@ def test_packed_sweep(c):
     pool = gla.gla_state_alloc(n_slots, H=c["H"])
     pool.view().copy_(to_dev(d["pool"], torch.float32))
     N = d["q"].shape[0]
-    with _Env("GLA_FWD_SEGMENTS", c["seg"]):
-        o = gla.gla_chunk_fwd_varlen(to_dev(d["q"], TDT[c["in_dt"]]), to_dev(d["k"], TDT[c["in_dt"]]),
-                                     to_dev(d["v"], TDT[c["in_dt"]]), to_dev(d["g"], torch.float32),
-                                     torch.from_numpy(d["cu_seqlens"]).to(dev()), max(1, max(c["lengths"])),
-                                     pool, torch.from_numpy(d["slot_idx"]).to(dev()), init_from_pool=c["init"],
-                                     out_dtype=TDT[c["out_dt"]])
-        torch.cuda.synchronize()
+    o = gla.gla_chunk_fwd_varlen(to_dev(d["q"], TDT[c["in_dt"]]), to_dev(d["k"], TDT[c["in_dt"]]),
+                                 to_dev(d["v"], TDT[c["in_dt"]]), to_dev(d["g"], torch.float32),
+                                 torch.from_numpy(d["cu_seqlens"]).to(dev()), max(1, max(c["lengths"])),
+                                 pool, torch.from_numpy(d["slot_idx"]).to(dev()), init_from_pool=c["init"],
+                                 out_dtype=TDT[c["out_dt"]], segments=c["seg"])
+    torch.cuda.synchronize()
     o_ref, pool_ref = oracle.forward_packed(d["q"], d["k"], d["v"], d["g"], d["cu_seqlens"], d["pool"],
                                             d["slot_idx"], c["init"])
     if N:
