@@ -200,6 +200,30 @@ gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k,
                          float* S_T, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gla_chunk_fwd for callers that cannot allocate device memory or hand over
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments and results as gla_chunk_fwd
+ * (bitwise: the same kernels and plan), without ws/ws_bytes.  The workspace
+ * of a segmented plan lives in a static device array of
+ * GLA_NOALLOC_SCRATCH_BYTES that the library owns; each device the library
+ * runs on holds its own copy until the process ends.  The call allocates
+ * nothing and calls no allocating routine; its first call on a device looks
+ * the array's address up (no allocation, no launch).  Every call on a device
+ * shares that device's array, so calls that overlap in time on one device
+ * (different streams, or several host threads) race and give undefined
+ * results: serialise them.  GLA_DEBUG's device checks are not run here (they
+ * synchronise and allocate).  Every plan the library picks by itself
+ * (dims->segments = 0) fits the array; a plan that needs more than
+ * GLA_NOALLOC_SCRATCH_BYTES (a large forced segment count) returns
+ * GLA_ERR_UNSUPPORTED naming both sizes, before any launch.
+ * Errors: as gla_chunk_fwd, plus UNSUPPORTED for that case and DEVICE when
+ * the array's address cannot be resolved. */
+#define GLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const void* q, const void* k,
+                                 const void* v, const float* g, const float* S0,
+                                 void* o, float* S_T, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Element strides of a token tensor: element i of the row of (batch b, token
  * t, head h) is at p[b*batch + t*token + h*head + i] (each row contiguous).
  * For g, which has one float per (b, t, h), the same with i = 0. */

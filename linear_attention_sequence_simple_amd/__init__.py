@@ -7,6 +7,7 @@ functions carry the names of the C entry points (include/gla.h):
     gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None)        -> (o, S_T)
     gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, o=None)
                                                                -> (o, S_T)
+    gla_chunk_fwd_noalloc(q, k, v, g, o, S0=None, S_T=None)    -> (o, S_T)
     gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool,
                          slot_idx=None, init_from_pool=False,
                          out_dtype=None)                       -> o
@@ -36,7 +37,7 @@ import os
 import torch
 
 __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GLA_OP_FWD_VARLEN_Q16", "GlaError", "GlaDims",
-           "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
+           "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_noalloc", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_write",
            "gla_state_read", "GLA_STATE_F32", "GLA_STATE_Q16",
            "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS",
@@ -52,7 +53,7 @@ EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slot
            "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
            "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_q16_ptrs",
-           "gla_state_write", "gla_state_read", "gla_status_str", "gla_last_error"]
+           "gla_state_write", "gla_state_read", "gla_status_str", "gla_last_error", "gla_chunk_fwd_noalloc"]
 
 
 class GlaError(RuntimeError):
@@ -99,6 +100,7 @@ def lib():
     L.gla_state_slot_bytes.restype = SZ
     L.gla_workspace_size.argtypes = [I32, ctypes.POINTER(GlaDims), ctypes.POINTER(SZ)]
     L.gla_chunk_fwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, SZ, P]
+    L.gla_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P]
     SP = ctypes.POINTER(GlaStrides)
     L.gla_chunk_fwd_strided.argtypes = [ctypes.POINTER(GlaDims), P, SP, P, SP, P, SP, P, SP, P, P, SP, P, P, SZ, P]
     L.gla_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GlaDims), I64, P, P, P, P, P, P, P, I32, P, P, SZ, P]
@@ -114,7 +116,7 @@ def lib():
     L.gla_status_str.argtypes = [I32]
     L.gla_status_str.restype = ctypes.c_char_p
     L.gla_last_error.restype = ctypes.c_char_p
-    for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd",
+    for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd", "gla_chunk_fwd_noalloc",
                  "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
                  "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_q16_ptrs", "gla_state_write",
                  "gla_state_read"):
@@ -206,6 +208,28 @@ def gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspac
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gla_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
                                _ptr(o), _ptr(S_T), _ptr(ws), nbytes, _stream()))
+    return o, S_T
+
+
+def gla_chunk_fwd_noalloc(q, k, v, g, o, S0=None, S_T=None, segments=None):
+    """gla_chunk_fwd without a workspace and without any allocation: the
+    caller passes o (and S_T, or None); a segmented plan uses the library's
+    static scratch array.  Returns (o, S_T)."""
+    B, T, H, _ = q.shape
+    dev = q.device
+    in_code = _dtype_code(q.dtype)
+    out_code = _dtype_code(o.dtype)
+    _need(q, "q", (B, T, H, DK), q.dtype, dev)
+    _need(k, "k", (B, T, H, DK), q.dtype, dev)
+    _need(v, "v", (B, T, H, DV), q.dtype, dev)
+    _need(g, "g", (B, T, H), torch.float32, dev)
+    _need(o, "o", (B, T, H, DV), o.dtype, dev)
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None:
+            _need(t, name, (B, H, DK, DV), torch.float32, dev)
+    dims = _dims(B, T, H, in_code, out_code, segments)
+    _check(lib().gla_chunk_fwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
+                                       _ptr(o), _ptr(S_T), _stream()))
     return o, S_T
 
 

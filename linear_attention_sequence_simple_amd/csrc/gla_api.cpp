@@ -481,6 +481,60 @@ gla_status state_io(const gla_state* pool, int64_t n, const int32_t* slot_idx, f
 }
 
 
+gla_status check_fwd_args(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
+                          const float* S0, const void* o, const float* S_T) {
+  TRY(check_dims(dims));
+  TRY(check_ptr(q, "q", false));
+  TRY(check_ptr(k, "k", false));
+  TRY(check_ptr(v, "v", false));
+  TRY(check_ptr(g, "g", false));
+  TRY(check_ptr(S0, "S0", true));
+  TRY(check_ptr(o, "o", false));
+  TRY(check_ptr(S_T, "S_T", true));
+  return GLA_OK;
+}
+
+// The forward over dense [B,T,H,d] tensors with the plan's workspace at ws.
+hipError_t launch_fwd_dense(const gla_dims* dims, const FwdPlan& p, const void* q, const void* k, const void* v,
+                            const float* g, const float* S0, void* o, float* S_T, void* ws, hipStream_t st) {
+  WalkArgs a = fwd_args(dims, p, q, k, v, g, o, dims->T);
+  const int w = DV / p.ns;
+  return run_fwd(dims, p, a, state_plain(const_cast<float*>(S0), w), state_plain(S_T, w), ws, st);
+}
+
+// ---- Scratch of gla_chunk_fwd_noalloc: the segment plan's workspace in a
+// static device array, one copy per device, never allocated by the library.
+// Every call on a device shares its copy, so calls that overlap on one device
+// race; nothing in it needs to start at zero (pass 1 writes every segment
+// entry before the scan and the walks read it).
+constexpr size_t kScratchBytes = (size_t)GLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The array's device address on the current device, resolved once per
+// device with that device current (the array's name in host code is only a
+// stand-in for the symbol, never an address to pass to a kernel).
+gla_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  TRY(device_err(hipGetDevice(&dev), "hipGetDevice"));
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *out = it->second;
+    return GLA_OK;
+  }
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return fail(GLA_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+  }
+  addr[dev] = p;
+  *out = p;
+  return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -574,25 +628,29 @@ gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes) {
 
 gla_status gla_chunk_fwd(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
                          const float* S0, void* o, float* S_T, void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_dims(dims));
-  TRY(check_ptr(q, "q", false));
-  TRY(check_ptr(k, "k", false));
-  TRY(check_ptr(v, "v", false));
-  TRY(check_ptr(g, "g", false));
-  TRY(check_ptr(S0, "S0", true));
-  TRY(check_ptr(o, "o", false));
-  TRY(check_ptr(S_T, "S_T", true));
+  TRY(check_fwd_args(dims, q, k, v, g, S0, o, S_T));
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
   TRY(debug_checks((hipStream_t)stream, "gla_chunk_fwd", [&](int* f) {
     return debug_decay(g, dims->B, dims->T, dims->H, dims->T * dims->H, dims->H, 1, f, (hipStream_t)stream);
   }));
-  WalkArgs a = fwd_args(dims, p, q, k, v, g, o, dims->T);
-  const int w = DV / p.ns;
-  const hipError_t e = run_fwd(dims, p, a, state_plain(const_cast<float*>(S0), w), state_plain(S_T, w), ws,
-                               (hipStream_t)stream);
-  return device_err(e, "gla_chunk_fwd launch");
+  return device_err(launch_fwd_dense(dims, p, q, k, v, g, S0, o, S_T, ws, (hipStream_t)stream), "gla_chunk_fwd launch");
+}
+
+gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
+                                 const float* S0, void* o, float* S_T, void* stream) {
+  TRY(check_fwd_args(dims, q, k, v, g, S0, o, S_T));
+  const FwdPlan p = plan_fwd(dims);
+  if (p.ws_total > kScratchBytes)
+    return fail(GLA_ERR_UNSUPPORTED,
+                "gla_chunk_fwd_noalloc: this plan needs %zu bytes of scratch, more than the library's static "
+                "%zu-byte array; call gla_chunk_fwd with a workspace",
+                p.ws_total, kScratchBytes);
+  void* ws = nullptr;
+  if (p.ws_total > 0) TRY(scratch_ptr(&ws));
+  return device_err(launch_fwd_dense(dims, p, q, k, v, g, S0, o, S_T, ws, (hipStream_t)stream),
+                    "gla_chunk_fwd_noalloc launch");
 }
 
 gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q, const gla_strides* sq, const void* k,

@@ -187,6 +187,20 @@ def test_strided_validation(L):
     assert call(sq=dense_q, sg=S(300 * 17, 17, 0)) == 1 and "g strides" in L.gla_last_error().decode()
 
 
+def test_noalloc_scratch_limit(L):
+    """gla_chunk_fwd_noalloc rejects a plan whose scratch exceeds the static
+    array before any HIP call; the library's own plans fit it."""
+    p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+    big = dims(B=64, T=8192, H=16, segments=64)
+    assert ws_size(L, gla.GLA_OP_FWD, big)[1] > 32 << 20
+    st = L.gla_chunk_fwd_noalloc(ctypes.byref(big), p, p, p, p, None, p, None, None)
+    assert st == 2 and "scratch" in L.gla_last_error().decode()
+    for kw in (dict(B=1, T=65536), dict(B=1, T=262144, H=1), dict(B=2, T=131072, H=1), dict(B=1, T=2048, H=16,
+               in_dtype=gla.GLA_F32), dict(B=1, T=1 << 20, H=16), dict(B=3, T=4096, H=7, in_dtype=gla.GLA_F32)):
+        assert ws_size(L, gla.GLA_OP_FWD, dims(**kw))[1] <= 32 << 20, kw
+    assert L.gla_chunk_fwd_noalloc(None, p, p, p, p, None, p, None, None) == 1
+
+
 def test_backward_length_limit(L):
     p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
     d = dims(B=1, T=131_073, H=1)
