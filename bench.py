@@ -14,9 +14,11 @@ resident in HBM.  The same line carries, measured in the same run:
   packed    serving prefill: 16 prompts of 2,048-8,192 tokens packed along
             one token axis, final states written into a 1,280-slot pool
   fused     the headline prefill reading q, k, v in place from the fused
-            [8, 2048, 9216] projection output (strided views, no copies)
+            [8, 2048, 9216] projection output (strided views, no copies),
+            and the same with the output gate o * SiLU(gate) fused in
   conv      causal depth-wise conv1d (width 4) + SiLU ahead of the mixer,
-            B=8, T=2048, D=3,072, bf16 in/out, history kept per sequence
+            B=8, T=2048, D=3,072, bf16 in/out, window of the last four inputs kept
+            per sequence (float32)
   fp32      prefill B=1, T=2048 with fp32 inputs and outputs
   roofline  the prefill walk kernel against the HBM roof (HIP events)
   mfma_util the prefill's MFMA utilisation beside its ceiling (what the HBM
@@ -597,14 +599,16 @@ def bench_packed(torch, gla, steps, warmup):
 
 def bench_fused(torch, gla, steps, warmup):
     """The headline prefill on views of one [B, T, 9216] buffer holding every
-    head's q, k, v and gate per token (blocked by projection)."""
-    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=0)
+    head's q, k, v and gate per token (blocked by projection), without and
+    with the output gate o * SiLU(gate) applied in the walk's epilogue."""
+    d = gen.make_inputs("fwd_bf16_b8_t2048", seed=0, with_gate=True)
     B, T = d["meta"]["B"], d["meta"]["T"]
     dev = torch.device("cuda", 0)
     buf = torch.zeros((B, T, H * (2 * DK + 2 * DV)), dtype=torch.bfloat16, device=dev)
     views = (buf[..., :H * DK].unflatten(-1, (H, DK)), buf[..., H * DK:2 * H * DK].unflatten(-1, (H, DK)),
              buf[..., 2 * H * DK:2 * H * DK + H * DV].unflatten(-1, (H, DV)))
-    for view, name in zip(views, ("q", "k", "v")):
+    gate = buf[..., 2 * H * DK + H * DV:].unflatten(-1, (H, DV))
+    for view, name in zip(views + (gate,), ("q", "k", "v", "gate")):
         view.copy_(torch.from_numpy(d[name]).to(dev).to(torch.bfloat16))
     g = torch.from_numpy(d["g"]).to(dev)
     o = torch.empty((B, T, H, DV), dtype=torch.bfloat16, device=dev)
@@ -614,10 +618,27 @@ def bench_fused(torch, gla, steps, warmup):
     o_dense, S_dense = gla.gla_chunk_fwd(*(x.contiguous() for x in views), g, None, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     equal = bool(torch.equal(o, o_dense) and torch.equal(S_T, S_dense))
+    del o_dense, S_dense
+    y = torch.empty_like(o)
+    fn_g = lambda: gla.gla_chunk_fwd_strided(*views, g, None, out_dtype=torch.bfloat16, o=y, S_T=S_T, gate=gate)
+    ms_g, _ = _time_calls(torch, fn_g, steps, warmup, warm_ms=30)
+    torch.cuda.synchronize()
+    import oracle
+    bs, hs = [0, 7], [0, 15]
+    sub = lambda x: x[np.ix_(bs, range(T), hs)]
+    y_ref, _ = oracle.forward_gated(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]), sub(d["gate"]))
     nbytes = fwd_bytes(B, T, 2, 2)
+    nbytes_g = nbytes + B * T * H * DV * 2                 # the gate read once
     return {"workload": f"prefill B={B} T={T} H=16 bf16 in/out, q, k, v read in place from a [{B}, {T}, 9216] "
                         "fused projection buffer", "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gated": {"workload": "the same call with the output gate, o * SiLU(gate), the gate read in place "
+                                  "from the buffer's fourth part", "ms": ms_g,
+                      "tokens_per_s": B * T / (ms_g * 1e-3), "bytes": nbytes_g,
+                      "GBps": nbytes_g / (ms_g * 1e-3) / 1e9,
+                      "hbm_frac": nbytes_g / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "parity": {"y_bf16_out_over_bound": _bf16_out_ratio(sub(y.float().cpu().numpy()), y_ref, 1e-2),
+                                 "sample": "(b,h) in {0,7}x{0,15}, all 2048 tokens"}},
             "parity": {"bitwise_equal_to_dense_call": equal}}
 
 
@@ -632,7 +653,7 @@ def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
     ys = [torch.empty_like(xs[0]) for _ in range(sets)]
     w = torch.from_numpy((r.standard_normal((D, 4)) * 0.5).astype(np.float32)).to(dev)
     bias = torch.from_numpy((r.standard_normal(D) * 0.1).astype(np.float32)).to(dev)
-    hist = torch.zeros((B, 3, D), dtype=torch.bfloat16, device=dev)
+    hist = torch.zeros((B, 4, D), dtype=torch.float32, device=dev)   # each sequence's window, float32
     it = [0]
 
     def fn():
@@ -640,20 +661,22 @@ def bench_conv(torch, gla, steps, warmup, B=8, T=2048, D=3072, sets=4):
         it[0] += 1
         gla.gla_conv1d_silu(xs[i], w, bias, conv_state=hist, init_from_state=True, y=ys[i])
     ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
-    # sampled parity: sequence 0 of set 0 from a zero history, against the oracle
+    # sampled parity: sequence 0 of set 0 from a zero window, against the oracle
     import oracle
     hist.zero_()
     gla.gla_conv1d_silu(xs[0], w, bias, conv_state=hist, init_from_state=True, y=ys[0])
     torch.cuda.synchronize()
     x0 = xs[0][0].float().cpu().numpy()
-    y_ref, h_ref = oracle.conv1d_silu(x0, w.cpu().numpy(), bias.cpu().numpy(), [0, T], np.zeros((1, 3, D)), None, True)
+    y_ref, h_ref = oracle.conv1d_silu(x0, w.cpu().numpy(), bias.cpu().numpy(), [0, T], np.zeros((1, 4, D)), None, True)
     parity = {"y_bf16_out_over_bound": _bf16_out_ratio(ys[0][0].float().cpu().numpy(), y_ref, 1e-5),
-              "history_bitwise": bool(np.array_equal(hist[0].float().cpu().numpy(), h_ref[0])),
+              "window_bitwise": bool(np.array_equal(hist[0].cpu().numpy(), h_ref[0])),
               "sample": f"sequence 0, all {D} channels, {T} tokens"}
-    # x read and y written once (2 B each per token-channel), the history read and written
-    nbytes = B * T * D * 4 + 2 * B * 3 * D * 2
+    # x read and y written once (2 B each per token-channel); of each
+    # sequence's float32 window three rows read and four written
+    nbytes = B * T * D * 4 + B * (3 + 4) * D * 4
     return {"workload": f"causal depth-wise conv1d width 4 + SiLU, B={B} T={T} D={D}, bf16 in/out, "
-                        f"history kept per sequence; calls cycle over {sets} input/output sets",
+                        f"float32 window of the last four inputs kept per sequence; calls cycle over {sets} "
+                        "input/output sets",
             "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes, "kernels_per_call": 1,
             "parity": parity}

@@ -27,7 +27,7 @@ __all__ = [
 ]
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "g": 3, "S0": 4, "dO": 5, "u_head": 6,
-              "dS_T": 7, "slot": 8, "len": 9}
+              "dS_T": 7, "slot": 8, "len": 9, "gate": 10}
 
 # name -> description.  "g" names the log-decay recipe (see make_g),
 # "S0" the initial-state recipe ("zero" or "normal0.1": N(0, 0.1^2)).
@@ -106,12 +106,12 @@ def _normal(workload_id, tensor, seed, shape, scale):
 
 def make_inputs(workload: str, seed: int = 0, B=None, T=None, H=None, dk=None,
                 dv=None, g=None, S0=None, dtype=None, with_dO=False,
-                with_dS_T=False) -> dict:
+                with_dS_T=False, with_gate=False) -> dict:
     """Inputs of a prefill/backward workload as float32 numpy arrays.
 
     Keyword arguments override the workload's sizes or recipes (reduced
-    shapes for parity tests).  For bf16 workloads q, k, v (and dO, dS_T are
-    left fp32 except dO) hold bf16-representable values.
+    shapes for parity tests).  For bf16 workloads q, k, v, dO and the gate
+    hold bf16-representable values (S0 and dS_T stay float32).
     """
     w = dict(WORKLOADS[workload])
     for key, val in (("B", B), ("T", T), ("H", H), ("dk", dk), ("dv", dv),
@@ -136,8 +136,11 @@ def make_inputs(workload: str, seed: int = 0, B=None, T=None, H=None, dk=None,
         out["dO"] = _normal(wid, "dO", seed, (Bn, Tn, Hn, V), 1.0)
     if with_dS_T:
         out["dS_T"] = _normal(wid, "dS_T", seed, (Bn, Hn, K, V), 0.1)
+    if with_gate:
+        # the output gate of the fused projection, [B, T, H, dv]: N(0, 1)
+        out["gate"] = _normal(wid, "gate", seed, (Bn, Tn, Hn, V), 1.0)
     if w["dtype"] == "bf16":
-        for key in ("q", "k", "v", "dO"):
+        for key in ("q", "k", "v", "dO", "gate"):
             if key in out:
                 out[key] = bf16_round(out[key])
     out["meta"] = w

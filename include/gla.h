@@ -43,8 +43,9 @@
  *    kernels.  Such a call synchronises and allocates one word per device on
  *    first use, so it cannot be captured in a graph.  The checks of calls
  *    from several host threads run one at a time (the flag word is shared);
- *    without GLA_DEBUG nothing is checked on the device.  The convolution's history tensor is
- *    the caller's, so only its negative and repeated slot indices are caught.
+ *    without GLA_DEBUG nothing is checked on the device.  The convolution's window tensor
+ *    (gla_conv1d_silu) is the caller's, so only its negative and repeated
+ *    slot indices are caught.
  */
 #ifndef GLA_H
 #define GLA_H
@@ -173,6 +174,37 @@ gla_status gla_state_write(gla_state* pool, int64_t n, const int32_t* slot_idx,
 gla_status gla_state_read(const gla_state* pool, int64_t n, const int32_t* slot_idx,
                           float* S, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * A layer's whole per-sequence state in one slot.  The pages put 29.5 MB of
+ * fixed state per sequence ("Cómo i14 llevó Laplace 3B a AWS Trainium2",
+ * "Introducción"; "AWS serve Laplace 3B di i14 con uno stato fisso di 29,5
+ * MB", "Lo stato di Laplace 3B resta fisso durante l'inferenza") across 24
+ * layers.  Each layer carries the mixer's state and the window of the causal
+ * convolution ahead of it ("Diseño esencial de Laplace 3B": width 4 over
+ * D = 3,072 channels); with a float32 mixer state (16 x 96 x 192) and a
+ * float32 window of 4 x 3,072 a layer-slot is 1,228,800 B and 24 of them are
+ * 29,491,200 B, the printed 29.5 MB.
+ *
+ * gla_state_alloc_conv: a pool as gla_state_alloc (format GLA_STATE_F32) or
+ * gla_state_alloc_q16 (GLA_STATE_Q16) whose slots also hold a zero-filled
+ * float32 window [4, conv_D] (one allocation; conv_D a multiple of 8 in
+ * [8, 65536]).  gla_conv1d_silu_pool reads and writes it; the mixer calls
+ * use the pool as any other.  Errors: as gla_state_alloc, plus UNSUPPORTED
+ * for conv_D and INVALID_ARGUMENT for an unknown format.
+ * gla_state_conv_channels: the pool's conv_D (0 without a window or NULL).
+ * gla_state_conv_ptr: device pointer to slot `slot`'s window ([4, conv_D]
+ *   float32, rows as in gla_conv1d_silu), NULL without a window or out of range.
+ * gla_state_seq_bytes: bytes of one slot of such a pool, mixer state plus
+ *   window (conv_D = 0: the mixer state alone); 0 for invalid sizes.
+ */
+gla_status gla_state_alloc_conv(int64_t n_slots, int32_t H, int32_t dk, int32_t dv,
+                                int32_t format, int32_t conv_D, void* stream,
+                                gla_state** out);
+int32_t gla_state_conv_channels(const gla_state* pool);
+float* gla_state_conv_ptr(const gla_state* pool, int64_t slot);
+size_t gla_state_seq_bytes(int32_t H, int32_t dk, int32_t dv, int32_t format,
+                           int32_t conv_D);
+
 /* Workspace bytes that gla_chunk_fwd (op = GLA_OP_FWD) or gla_chunk_bwd
  * (op = GLA_OP_BWD) needs for `dims`, or gla_chunk_fwd_varlen into a 16-bit
  * pool (op = GLA_OP_FWD_VARLEN_Q16: the forward's bytes plus a float32 state
@@ -237,16 +269,27 @@ typedef struct {
  * "Diseño esencial de Laplace 3B"), and o written into a wider buffer.
  *   sq, sk, sv, so : strides of q, k, v, o (NULL: the dense [B,T,H,d] layout)
  *   sg   : strides of g (NULL: dense [B,T,H])
- * Strides are positive; for q, k, v and o they are multiples of 16 bytes, and
- * token and head strides times 32 rows stay under 2^31 bytes
- * (INVALID_ARGUMENT otherwise).  q, k, v and o are 16-byte aligned, g 4-byte
- * aligned.  Views must not overlap o or S_T (caller contract).  Everything
- * else is as gla_chunk_fwd, whose workspace size applies. */
+ *   gate : NULL, or the gate of that projection, [B,T,H,dv] in in_dtype
+ *          (sgate: its strides, NULL for the dense layout).  When given, the
+ *          output is gated in the walk's epilogue before it is stored:
+ *              o_t[h][c] = (q_t S_t)[h][c] * SiLU(gate_t[h][c]),
+ *              SiLU(a) = a / (1 + exp(-a)).
+ *          The pages split the projection into q, k, v and this gate (dv
+ *          wide per head) without printing how it meets the mixer's output;
+ *          the elementwise SiLU gate is this library's reading of it, with
+ *          the activation the same section names.  Computed in float32
+ *          from the float32 output; S_T is not gated.
+ * Strides are positive; for q, k, v, gate and o they are multiples of 16
+ * bytes, and token and head strides times 32 rows stay under 2^31 bytes
+ * (INVALID_ARGUMENT otherwise).  q, k, v, gate and o are 16-byte aligned, g
+ * 4-byte aligned.  Views must not overlap o or S_T (caller contract).
+ * Everything else is as gla_chunk_fwd, whose workspace size applies. */
 gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q,
                                  const gla_strides* sq, const void* k,
                                  const gla_strides* sk, const void* v,
                                  const gla_strides* sv, const float* g,
-                                 const gla_strides* sg, const float* S0, void* o,
+                                 const gla_strides* sg, const void* gate,
+                                 const gla_strides* sgate, const float* S0, void* o,
                                  const gla_strides* so, float* S_T, void* ws,
                                  size_t ws_bytes, void* stream);
 
@@ -353,21 +396,24 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k,
  *     a_t[c] = bias[c] + sum_{j=0..3} w[c][j] * x_{t-3+j}[c]
  *     y_t[c] = a_t[c] / (1 + exp(-a_t[c]))
  * so w[c][3] weights the current token.  Tokens before a sequence's first
- * come from its history in conv_state (init_from_state = 1) or are zero.
+ * come from its window in conv_state (init_from_state = 1) or are zero.
  *
- *   B, T, D : B sequences of at most T tokens, D channels (a multiple of 8;
- *             3,072 in the pages' model)
+ *   B, T, D : B sequences of at most T tokens, D channels (a multiple of 8 in
+ *             [8, 65536]; 3,072 in the pages' model)
  *   cu_seqlens : NULL: x and y are [B, T, D], every sequence T tokens long.
  *             Else device int32 [B + 1]: x and y are [total_tokens, D] and
  *             sequence b is rows [cu_seqlens[b], cu_seqlens[b+1]), with the
  *             clamping and caller contract of gla_chunk_fwd_varlen.
  *   x    : in_dtype            y : out_dtype (same layout as x)
  *   w    : [D, 4] float32      bias : [D] float32 or NULL (zero)
- *   conv_state : [n_slots, 3, D] in_dtype or NULL; row m of a slot holds
- *             the input three-minus-m tokens back.  When given, each
- *             sequence's slot (slot_idx[b], device int32 [B], or b when NULL;
- *             in range and distinct, a caller contract) receives the last
- *             three inputs of its history followed by its tokens.  One
+ *   conv_state : [n_slots, 4, D] float32 or NULL: each slot is the window of
+ *             the filter's width, row m holding the input four-minus-m tokens
+ *             back (row 3 the newest; row 0 is kept for the window's full
+ *             width but not read).  When given, each sequence's slot
+ *             (slot_idx[b], device int32 [B], or b when NULL; in range and
+ *             distinct, a caller contract) receives the last four rows of its
+ *             window (zeros without init_from_state) followed by its tokens;
+ *             an empty sequence with init_from_state keeps its window.  One
  *             decode step is T = 1.
  * Errors: INVALID_ARGUMENT (NULL or misaligned pointers, B or T < 1,
  * init_from_state without conv_state), UNSUPPORTED (D), DEVICE.
@@ -375,9 +421,25 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k,
 gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype,
                            int32_t out_dtype, const int32_t* cu_seqlens,
                            int64_t total_tokens, const void* x, const float* w,
-                           const float* bias, void* conv_state,
+                           const float* bias, float* conv_state,
                            const int32_t* slot_idx, int32_t init_from_state,
                            void* y, void* stream);
+
+/* gla_conv1d_silu with the windows kept in a pool's slots (a pool made by
+ * gla_state_alloc_conv), so that one slot holds a sequence's whole state for
+ * the layer: the convolution's window and the mixer's state, addressed by the
+ * same slot indices as gla_chunk_fwd_varlen and gla_recurrent_step.  D is the
+ * pool's conv_D.  Arguments otherwise as gla_conv1d_silu (init_from_pool
+ * plays init_from_state).  Under GLA_DEBUG slot indices are checked against
+ * the pool's slot count.
+ * Errors: as gla_conv1d_silu, plus INVALID_ARGUMENT for a NULL pool, a pool
+ * without a window, B > slots when slot_idx is NULL. */
+gla_status gla_conv1d_silu_pool(int64_t B, int64_t T, int32_t in_dtype,
+                                int32_t out_dtype, const int32_t* cu_seqlens,
+                                int64_t total_tokens, const void* x, const float* w,
+                                const float* bias, gla_state* pool,
+                                const int32_t* slot_idx, int32_t init_from_pool,
+                                void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Errors. */

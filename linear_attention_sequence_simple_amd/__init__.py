@@ -5,7 +5,7 @@ stream, every step of the computation runs in the library's kernels.  The
 functions carry the names of the C entry points (include/gla.h):
 
     gla_chunk_fwd(q, k, v, g, S0=None, out_dtype=None)        -> (o, S_T)
-    gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, o=None)
+    gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, o=None, gate=None)
                                                                -> (o, S_T)
     gla_chunk_fwd_noalloc(q, k, v, g, o, S0=None, S_T=None)    -> (o, S_T)
     gla_chunk_fwd_varlen(q, k, v, g, cu_seqlens, max_seqlen, pool,
@@ -19,6 +19,10 @@ functions carry the names of the C entry points (include/gla.h):
                     out_dtype=None)                            -> y
     gla_state_alloc(n_slots, H=16, dk=96, dv=192)             -> StatePool
     gla_state_alloc_q16(n_slots, H=16, dk=96, dv=192)         -> StatePool (16-bit)
+    gla_state_alloc_conv(n_slots, conv_D, H=16, dk=96, dv=192, fmt=GLA_STATE_F32)
+                                                              -> StatePool with a conv window per slot
+    gla_conv1d_silu_pool(x, w, pool, bias=None, slot_idx=None, init_from_pool=False,
+                         cu_seqlens=None, max_seqlen=None, out_dtype=None) -> y
     gla_state_format(pool)                                    -> GLA_STATE_F32 | GLA_STATE_Q16
     gla_state_write(pool, S, slot_idx=None)                   (float32 states into slots)
     gla_state_read(pool, n=None, slot_idx=None, S=None)       -> S float32
@@ -38,7 +42,8 @@ import torch
 
 __all__ = ["GLA_F32", "GLA_BF16", "GLA_OP_FWD", "GLA_OP_BWD", "GLA_OP_FWD_VARLEN_Q16", "GlaError", "GlaDims",
            "lib", "lib_path", "gla_chunk_fwd", "gla_chunk_fwd_noalloc", "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
-           "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_write",
+           "gla_conv1d_silu", "gla_conv1d_silu_pool", "gla_state_alloc_conv", "gla_state_alloc_q16",
+           "gla_state_format", "gla_state_write",
            "gla_state_read", "GLA_STATE_F32", "GLA_STATE_Q16",
            "gla_state_alloc", "gla_workspace_size", "StatePool", "EXPORTS",
            "chunk_fwd", "recurrent_step", "chunk_bwd"]
@@ -53,7 +58,9 @@ EXPORTS = ["gla_state_alloc", "gla_state_free", "gla_state_ptr", "gla_state_slot
            "gla_state_slot_bytes", "gla_workspace_size", "gla_chunk_fwd",
            "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
            "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_format", "gla_state_q16_ptrs",
-           "gla_state_write", "gla_state_read", "gla_status_str", "gla_last_error", "gla_chunk_fwd_noalloc"]
+           "gla_state_write", "gla_state_read", "gla_status_str", "gla_last_error", "gla_chunk_fwd_noalloc",
+           "gla_conv1d_silu_pool", "gla_state_alloc_conv", "gla_state_conv_channels", "gla_state_conv_ptr",
+           "gla_state_seq_bytes"]
 
 
 class GlaError(RuntimeError):
@@ -102,11 +109,20 @@ def lib():
     L.gla_chunk_fwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, SZ, P]
     L.gla_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P]
     SP = ctypes.POINTER(GlaStrides)
-    L.gla_chunk_fwd_strided.argtypes = [ctypes.POINTER(GlaDims), P, SP, P, SP, P, SP, P, SP, P, P, SP, P, P, SZ, P]
+    L.gla_chunk_fwd_strided.argtypes = [ctypes.POINTER(GlaDims), P, SP, P, SP, P, SP, P, SP, P, SP, P, P, SP, P, P,
+                                        SZ, P]
     L.gla_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GlaDims), I64, P, P, P, P, P, P, P, I32, P, P, SZ, P]
     L.gla_recurrent_step.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
     L.gla_chunk_bwd.argtypes = [ctypes.POINTER(GlaDims), P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.gla_conv1d_silu.argtypes = [I64, I64, I32, I32, I32, P, I64, P, P, P, P, P, I32, P, P]
+    L.gla_conv1d_silu_pool.argtypes = [I64, I64, I32, I32, P, I64, P, P, P, P, P, I32, P, P]
+    L.gla_state_alloc_conv.argtypes = [I64, I32, I32, I32, I32, I32, P, ctypes.POINTER(P)]
+    L.gla_state_conv_channels.argtypes = [P]
+    L.gla_state_conv_channels.restype = I32
+    L.gla_state_conv_ptr.argtypes = [P, I64]
+    L.gla_state_conv_ptr.restype = P
+    L.gla_state_seq_bytes.argtypes = [I32, I32, I32, I32, I32]
+    L.gla_state_seq_bytes.restype = SZ
     L.gla_state_alloc_q16.argtypes = [I64, I32, I32, I32, P, ctypes.POINTER(P)]
     L.gla_state_format.argtypes = [P]
     L.gla_state_format.restype = I32
@@ -118,8 +134,8 @@ def lib():
     L.gla_last_error.restype = ctypes.c_char_p
     for name in ("gla_state_alloc", "gla_state_free", "gla_workspace_size", "gla_chunk_fwd", "gla_chunk_fwd_noalloc",
                  "gla_chunk_fwd_strided", "gla_chunk_fwd_varlen", "gla_recurrent_step", "gla_chunk_bwd",
-                 "gla_conv1d_silu", "gla_state_alloc_q16", "gla_state_q16_ptrs", "gla_state_write",
-                 "gla_state_read"):
+                 "gla_conv1d_silu", "gla_conv1d_silu_pool", "gla_state_alloc_conv", "gla_state_alloc_q16",
+                 "gla_state_q16_ptrs", "gla_state_write", "gla_state_read"):
         getattr(L, name).restype = I32
     _LIB = L
     return L
@@ -248,9 +264,11 @@ def _view_strides(t, name, shape, dtype, device):
 
 
 def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, workspace=None, o=None,
-                          S_T=None, segments=None):
+                          S_T=None, segments=None, gate=None):
     """gla_chunk_fwd on views with any positive batch/token/head strides (for
-    example q, k, v sliced out of a fused projection output), rows contiguous."""
+    example q, k, v sliced out of a fused projection output), rows contiguous.
+    gate: None, or a [B,T,H,192] view in q's dtype; the output is then
+    o * SiLU(gate), applied before the store."""
     B, T, H, _ = q.shape
     dev = q.device
     in_code = _dtype_code(q.dtype)
@@ -259,6 +277,7 @@ def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, 
     sk = _view_strides(k, "k", (B, T, H, DK), q.dtype, dev)
     sv = _view_strides(v, "v", (B, T, H, DV), q.dtype, dev)
     sg = _view_strides(g, "g", (B, T, H), torch.float32, dev)
+    sgate = None if gate is None else _view_strides(gate, "gate", (B, T, H, DV), q.dtype, dev)
     if S0 is not None:
         _need(S0, "S0", (B, H, DK, DV), torch.float32, dev)
     if o is None:
@@ -273,6 +292,7 @@ def gla_chunk_fwd_strided(q, k, v, g, S0=None, out_dtype=None, want_state=True, 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     r = ctypes.byref
     _check(lib().gla_chunk_fwd_strided(r(dims), _ptr(q), r(sq), _ptr(k), r(sk), _ptr(v), r(sv), _ptr(g), r(sg),
+                                       _ptr(gate), None if sgate is None else r(sgate),
                                        _ptr(S0), _ptr(o), r(so), _ptr(S_T), _ptr(ws), nbytes, _stream()))
     return o, S_T
 
@@ -352,8 +372,9 @@ def gla_conv1d_silu(x, w, bias=None, conv_state=None, slot_idx=None, init_from_s
 
     x [B,T,D] (or [N,D] with int32 cu_seqlens [n_seq+1] on the device and
     max_seqlen); w [D,4] float32; bias [D] float32 or None; conv_state
-    [n_slots,3,D] in x's dtype or None (each sequence's history, updated in
-    place); slot_idx int32 [n_seq] on the device or None.  Returns y.
+    [n_slots,4,D] float32 or None (each sequence's window of its last four
+    inputs, updated in place); slot_idx int32 [n_seq] on the device or None.
+    Returns y.
     """
     dev = x.device
     in_code = _dtype_code(x.dtype)
@@ -374,9 +395,9 @@ def gla_conv1d_silu(x, w, bias=None, conv_state=None, slot_idx=None, init_from_s
     if bias is not None:
         _need(bias, "bias", (D,), torch.float32, dev)
     if conv_state is not None:
-        if conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (3, D):
-            raise ValueError(f"conv_state must be [n_slots, 3, {D}]")
-        _need(conv_state, "conv_state", tuple(conv_state.shape), x.dtype, dev)
+        if conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (4, D):
+            raise ValueError(f"conv_state must be [n_slots, 4, {D}]")
+        _need(conv_state, "conv_state", tuple(conv_state.shape), torch.float32, dev)
     if slot_idx is not None:
         _need(slot_idx, "slot_idx", (B,), torch.int32, dev)
     if y is None:
@@ -385,6 +406,42 @@ def gla_conv1d_silu(x, w, bias=None, conv_state=None, slot_idx=None, init_from_s
     _check(lib().gla_conv1d_silu(B, T, D, in_code, out_code, _ptr(cu_seqlens), total, _ptr(x), _ptr(w),
                                  _ptr(bias), _ptr(conv_state), _ptr(slot_idx), int(bool(init_from_state)),
                                  _ptr(y), _stream()))
+    return y
+
+
+def gla_conv1d_silu_pool(x, w, pool, bias=None, slot_idx=None, init_from_pool=False, cu_seqlens=None,
+                         max_seqlen=None, out_dtype=None, y=None):
+    """gla_conv1d_silu with each sequence's window in its slot of `pool` (a
+    StatePool made with conv_D); x has pool.conv_D channels."""
+    dev = x.device
+    in_code = _dtype_code(x.dtype)
+    out_code = in_code if out_dtype is None else _dtype_code(out_dtype)
+    D = pool.conv_D
+    if not D:
+        raise ValueError("the pool has no convolution window (make it with gla_state_alloc_conv)")
+    if x.shape[-1] != D:
+        raise ValueError(f"x has {x.shape[-1]} channels, the pool's window {D}")
+    if cu_seqlens is None:
+        if x.dim() != 3:
+            raise ValueError("x must be [B, T, D] without cu_seqlens")
+        B, T, total = x.shape[0], x.shape[1], x.shape[0] * x.shape[1]
+    else:
+        if x.dim() != 2 or max_seqlen is None:
+            raise ValueError("x must be [N, D] with cu_seqlens, and max_seqlen must be given")
+        B, T, total = cu_seqlens.numel() - 1, int(max_seqlen), x.shape[0]
+        _need(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32, dev)
+    _need(x, "x", tuple(x.shape), x.dtype, dev)
+    _need(w, "w", (D, 4), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (D,), torch.float32, dev)
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", (B,), torch.int32, dev)
+    if y is None:
+        y = torch.empty(tuple(x.shape), dtype=_torch_dtype(out_code), device=dev)
+    _need(y, "y", tuple(x.shape), _torch_dtype(out_code), dev)
+    _check(lib().gla_conv1d_silu_pool(B, T, in_code, out_code, _ptr(cu_seqlens), total, _ptr(x), _ptr(w),
+                                      _ptr(bias), pool.handle, _ptr(slot_idx), int(bool(init_from_pool)),
+                                      _ptr(y), _stream()))
     return y
 
 
@@ -401,13 +458,17 @@ class StatePool:
     (fmt GLA_STATE_F32) or 16-bit mantissas with one exponent per state column
     (GLA_STATE_Q16)."""
 
-    def __init__(self, n_slots, H=16, dk=DK, dv=DV, fmt=GLA_STATE_F32):
+    def __init__(self, n_slots, H=16, dk=DK, dv=DV, fmt=GLA_STATE_F32, conv_D=0):
         handle = ctypes.c_void_p()
-        alloc = lib().gla_state_alloc_q16 if fmt == GLA_STATE_Q16 else lib().gla_state_alloc
-        _check(alloc(n_slots, H, dk, dv, _stream(), ctypes.byref(handle)))
+        if conv_D:
+            _check(lib().gla_state_alloc_conv(n_slots, H, dk, dv, fmt, conv_D, _stream(), ctypes.byref(handle)))
+        else:
+            alloc = lib().gla_state_alloc_q16 if fmt == GLA_STATE_Q16 else lib().gla_state_alloc
+            _check(alloc(n_slots, H, dk, dv, _stream(), ctypes.byref(handle)))
         self._h = handle
         self.n_slots, self.H, self.dk, self.dv = n_slots, H, dk, dv
         self.fmt = lib().gla_state_format(handle)
+        self.conv_D = lib().gla_state_conv_channels(handle)
         self.device = torch.device("cuda", torch.cuda.current_device())
 
     @property
@@ -441,6 +502,19 @@ class StatePool:
             raise TypeError("a 16-bit pool has no float32 view: use q16_views() or gla_state_read")
         return torch.as_tensor(self, device=self.device)
 
+    def conv_view(self) -> torch.Tensor:
+        """The convolution windows [n_slots, 4, conv_D] float32 (no copy)."""
+        if not self.conv_D:
+            raise TypeError("the pool has no convolution window")
+        p = lib().gla_state_conv_ptr(self.handle, 0)
+        arr = _DeviceArray(p, (self.n_slots, 4, self.conv_D), "<f4")
+        return torch.as_tensor(arr, device=self.device)
+
+    @property
+    def seq_bytes(self) -> int:
+        """Bytes of one slot: the mixer state and the convolution window."""
+        return lib().gla_state_seq_bytes(self.H, self.dk, self.dv, self.fmt, self.conv_D)
+
     def q16_views(self):
         """(mantissas int16 [n_slots,H,dk,dv], exponents int32 [n_slots,H,dv])
         aliasing a 16-bit pool (no copy)."""
@@ -468,6 +542,12 @@ def gla_state_alloc(n_slots, H=16, dk=DK, dv=DV) -> StatePool:
 
 def gla_state_alloc_q16(n_slots, H=16, dk=DK, dv=DV) -> StatePool:
     return StatePool(n_slots, H, dk, dv, fmt=GLA_STATE_Q16)
+
+
+def gla_state_alloc_conv(n_slots, conv_D, H=16, dk=DK, dv=DV, fmt=GLA_STATE_F32) -> StatePool:
+    """A pool whose slots hold a layer's mixer state (float32 or 16-bit) and
+    its convolution window [4, conv_D] float32."""
+    return StatePool(n_slots, H, dk, dv, fmt=fmt, conv_D=conv_D)
 
 
 def gla_state_format(pool: StatePool) -> int:

@@ -29,6 +29,8 @@ struct gla_state {
   int32_t format;              // gla_state_fmt
   int16_t* mant;               // GLA_STATE_Q16: mantissas [n_slots][H][dk][dv]
   int32_t* expo;               // and exponents [n_slots][H][dv]
+  float* conv;                 // the convolution's window [n_slots][4][conv_D] float32, or NULL
+  int32_t conv_D;              // its channels (0: no window)
   void* base;                  // the allocation
 };
 
@@ -358,6 +360,42 @@ BwdPlan plan_bwd(const gla_dims* d) {
   return p;
 }
 
+// fp32 backward workspace: the first dv-half's sums of dq and dk
+// ([B,T,H,DK] each), the float32 gradients when the outputs are bf16, q.dq
+// and k.dk ([B,T,H] each), the final forward state, the per-chunk sums of the
+// log-decay gradient.  Its walks run whole sequences (no segment plan).
+struct BwdF32Plan {
+  int n_chunks;
+  size_t off_adq, off_adk, off_fdq, off_fdk, off_rq, off_rk, off_st, off_r, ws_total;
+};
+
+BwdF32Plan plan_bwd_f32(const gla_dims* d) {
+  BwdF32Plan p{};
+  p.n_chunks = (int)((d->T + CH - 1) / CH);
+  const int64_t BH = d->B * d->H;
+  const size_t part = align256((size_t)d->B * d->T * d->H * DK * sizeof(float));
+  const size_t tok = align256((size_t)d->B * d->T * d->H * sizeof(float));
+  const bool bf16_out = d->out_dtype == GLA_BF16;
+  size_t off = 0;
+  p.off_adq = off; off += part;
+  p.off_adk = off; off += part;
+  p.off_fdq = off; off += bf16_out ? part : 0;
+  p.off_fdk = off; off += bf16_out ? part : 0;
+  p.off_rq = off; off += tok;
+  p.off_rk = off; off += tok;
+  p.off_st = off; off += align256((size_t)BH * kStateElems * sizeof(float));
+  p.off_r = off; off += align256((size_t)BH * (p.n_chunks + 1) * sizeof(float));
+  p.ws_total = off;
+  return p;
+}
+
+gla_status check_bwd_f32_plan(const gla_dims* d) {
+  if (d->segments > 1)
+    return fail(GLA_ERR_UNSUPPORTED, "the fp32 backward walks whole sequences: segments must be 0 or 1 (got %d)",
+                d->segments);
+  return GLA_OK;
+}
+
 // A view with caller strides (elements), in dv-slices of `slice_w` columns.
 TokView strided_view(const void* p, const gla_strides& s, int slice_w) {
   TokView v;
@@ -426,21 +464,41 @@ hipError_t run_fwd(const gla_dims* dims, const FwdPlan& p, WalkArgs a, StateView
 }
 
 
-// A pool of n_slots states in `format`, zero-filled in stream order (zero
+gla_status check_conv_D(int32_t D) {
+  if (D < 8 || D % 8 != 0 || D > (1 << 16))
+    return fail(GLA_ERR_UNSUPPORTED, "D must be a multiple of 8 in [8, 65536] (got %d)", D);
+  return GLA_OK;
+}
+
+// Bytes of one slot: the mixer state in `format` and the convolution's
+// window of conv_D channels (conv_D = 0: none).
+size_t slot_bytes(int32_t H, int32_t dk, int32_t dv, int32_t format, int32_t conv_D) {
+  const size_t mixer = format == GLA_STATE_Q16 ? (size_t)H * (dk * dv * sizeof(int16_t) + dv * sizeof(int32_t))
+                                               : (size_t)H * dk * dv * sizeof(float);
+  return mixer + (size_t)CONV_WIN * conv_D * sizeof(float);
+}
+
+// A pool of n_slots states in `format` (and, with conv_D > 0, a float32
+// convolution window [4][conv_D] per slot), zero-filled in stream order (zero
 // mantissas and exponents read as zero states too).
-gla_status alloc_pool(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, int32_t format, void* stream,
-                      gla_state** out) {
+gla_status alloc_pool(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, int32_t format, int32_t conv_D,
+                      void* stream, gla_state** out) {
   if (!out) return fail(GLA_ERR_INVALID_ARGUMENT, "out must not be NULL");
   *out = nullptr;
   if (n_slots < 1) return fail(GLA_ERR_INVALID_ARGUMENT, "n_slots must be >= 1 (got %lld)", (long long)n_slots);
   TRY(check_heads(H, dk, dv));
+  if (format != GLA_STATE_F32 && format != GLA_STATE_Q16)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "format must be GLA_STATE_F32 or GLA_STATE_Q16 (got %d)", format);
+  if (conv_D != 0) TRY(check_conv_D(conv_D));
   const bool q16 = format == GLA_STATE_Q16;
   const size_t slot = q16 ? (size_t)H * dk * dv * sizeof(int16_t) : gla_state_slot_bytes(H, dk, dv);
-  if ((size_t)n_slots > ((size_t)1 << 46) / slot)
+  if ((size_t)n_slots > ((size_t)1 << 46) / slot_bytes(H, dk, dv, format, conv_D))
     return fail(GLA_ERR_OUT_OF_MEMORY, "pool of %lld slots is too large", (long long)n_slots);
   const size_t mant_bytes = (size_t)n_slots * slot;
   const size_t expo_off = q16 ? align256(mant_bytes) : mant_bytes;
-  const size_t bytes = q16 ? expo_off + (size_t)n_slots * H * dv * sizeof(int32_t) : mant_bytes;
+  const size_t mixer_bytes = q16 ? expo_off + (size_t)n_slots * H * dv * sizeof(int32_t) : mant_bytes;
+  const size_t conv_off = align256(mixer_bytes);
+  const size_t bytes = conv_D ? conv_off + (size_t)n_slots * CONV_WIN * conv_D * sizeof(float) : mixer_bytes;
   int dev = 0;
   TRY(device_err(hipGetDevice(&dev), "hipGetDevice"));
   void* p = nullptr;
@@ -455,7 +513,8 @@ gla_status alloc_pool(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, int32_
     return device_err(e, "hipMemsetAsync");
   }
   gla_state* s = new gla_state{q16 ? nullptr : (float*)p, n_slots, H, dk, dv, dev, format,
-                               q16 ? (int16_t*)p : nullptr, q16 ? (int32_t*)((char*)p + expo_off) : nullptr, p};
+                               q16 ? (int16_t*)p : nullptr, q16 ? (int32_t*)((char*)p + expo_off) : nullptr,
+                               conv_D ? (float*)((char*)p + conv_off) : nullptr, conv_D, p};
   *out = s;
   return ok();
 }
@@ -535,6 +594,111 @@ gla_status scratch_ptr(void** out) {
   return GLA_OK;
 }
 
+// The backward with fp32 inputs: the bf16 path's walks on the fp32 matrix
+// cores.  dq and dk contract over the 192 value columns as two 96-column
+// halves (the walk's key width), the second adding the first's sums; their
+// values (k for dq, q for dk) are walked in three 32-column slices, and dv in
+// three 64-column slices.  Whole sequences, no segment plan.
+gla_status bwd_f32(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g, const float* S0,
+                   const void* dO, const float* dS_T, void* dq, void* dk, void* dv, float* dg, float* dS0, void* ws,
+                   size_t ws_bytes, void* stream) {
+  TRY(check_bwd_f32_plan(dims));
+  const BwdF32Plan p = plan_bwd_f32(dims);
+  if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
+  TRY(check_ptr(ws, "ws", false));
+  if (p.n_chunks > 1024) return fail(GLA_ERR_UNSUPPORTED, "the backward supports at most 1024 chunks (T <= 131072)");
+  hipStream_t st = (hipStream_t)stream;
+  TRY(debug_checks(st, "gla_chunk_bwd", [&](int* f) {
+    return debug_decay(g, dims->B, dims->T, dims->H, dims->T * dims->H, dims->H, 1, f, st);
+  }));
+  char* w = (char*)ws;
+  const int64_t BH = dims->B * dims->H;
+  const bool bf16_out = dims->out_dtype == GLA_BF16;
+  float* adq = (float*)(w + p.off_adq);
+  float* adk = (float*)(w + p.off_adk);
+  float* fdq = bf16_out ? (float*)(w + p.off_fdq) : (float*)dq;
+  float* fdk = bf16_out ? (float*)(w + p.off_fdk) : (float*)dk;
+  float* rq = (float*)(w + p.off_rq);
+  float* rk = (float*)(w + p.off_rk);
+  float* S_T = (float*)(w + p.off_st);
+  constexpr int hw = 96, sw = 32;                 // dv-half and value-slice widths
+  const int nq = DK / sw;                         // value slices of dq and dk walks
+  const SegPlan whole{nq, 1, p.n_chunks, p.n_chunks, 1};
+  // states of the dq and dk walks: element (x = column of a dv-half, y =
+  // row of S) of value slice s, i.e. S[32 s + y][half + x]
+  auto tview = [&](const float* base) { return StateView{const_cast<float*>(base), kStateElems, 0, (int64_t)sw * DV, 1, DV}; };
+  auto common = [&](WalkArgs& a, bool backwards) {
+    a.g = backwards ? g + (dims->T - 1) * dims->H : g;
+    a.gsb = dims->T * dims->H;
+    a.gsh = 1;
+    a.gst = backwards ? -(int64_t)dims->H : dims->H;
+    a.gshift = backwards ? 1 : 0;
+    a.B = dims->B;
+    a.T = dims->T;
+    a.H = dims->H;
+  };
+  hipError_t e = hipSuccess;
+  for (int hh = 0; hh < 2 && e == hipSuccess; ++hh) {
+    // dq: forward recurrence with keys a dv-half of v, values k, queries the
+    // same half of dO; its state is S^T restricted to the half
+    WalkArgs f{};
+    f.X = shifted(tok_view(v, 4, dims, DV, 0, false), (int64_t)hh * hw, 4);
+    f.Y = tok_view(k, 4, dims, DK, sw, false);
+    f.Q = shifted(tok_view(dO, 4, dims, DV, 0, false), (int64_t)hh * hw, 4);
+    f.O = tok_view(hh == 0 ? adq : fdq, 4, dims, DK, sw, false);
+    if (hh == 1) f.acc = tok_view(adq, 4, dims, DK, sw, false);
+    common(f, false);
+    const StateView fz0 = shifted(tview(S0), (int64_t)hh * hw);
+    const StateView fzT = shifted(tview(dS_T ? S_T : nullptr), (int64_t)hh * hw);
+    e = walk_segments(f, WV_OUT_F32_NC1, whole, S0 ? fz0 : StateView{}, dS_T ? fzT : StateView{}, BH, st);
+    if (e != hipSuccess) break;
+    // dk: backward in time, keys the half of dO, values q, queries the same
+    // half of v; its state is the state gradient's transpose
+    WalkArgs r{};
+    r.X = shifted(tok_view(dO, 4, dims, DV, 0, true), (int64_t)hh * hw, 4);
+    r.Y = tok_view(q, 4, dims, DK, sw, true);
+    r.Q = shifted(tok_view(v, 4, dims, DV, 0, true), (int64_t)hh * hw, 4);
+    r.O = tok_view(hh == 0 ? adk : fdk, 4, dims, DK, sw, true);
+    if (hh == 1) r.acc = tok_view(adk, 4, dims, DK, sw, true);
+    common(r, true);
+    const StateView rz0 = shifted(tview(dS_T), (int64_t)hh * hw);
+    e = walk_segments(r, WV_OUT_F32_NC1, whole, dS_T ? rz0 : StateView{}, StateView{}, BH, st);
+  }
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq/dk walks");
+  // dv: backward in time, keys q, values dO (64-column slices), queries k;
+  // the final state is the gradient leaving the first token
+  {
+    const int dw = 64;
+    WalkArgs a{};
+    a.X = tok_view(q, 4, dims, DK, 0, true);
+    a.Y = tok_view(dO, 4, dims, DV, dw, true);
+    a.Q = tok_view(k, 4, dims, DK, 0, true);
+    a.O = tok_view(dv, bf16_out ? 2 : 4, dims, DV, dw, true);
+    common(a, true);
+    const SegPlan whole_v{DV / dw, 1, p.n_chunks, p.n_chunks, 1};
+    e = walk_segments(a, bf16_out ? WV_FWD_OUT_F32_BF16 : WV_FWD_OUT_F32_F32, whole_v, state_plain(const_cast<float*>(dS_T), dw),
+                      state_plain(dS0, dw), BH, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dv walk");
+  }
+  RowDotsArgs rd{(const float*)q, (const float*)k, fdq, fdk, rq, rk, bf16_out ? (__bf16*)dq : nullptr,
+                 bf16_out ? (__bf16*)dk : nullptr, dims->B * dims->T * dims->H};
+  e = launch_row_dots(rd, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd row dots");
+  BwdFinishArgs fa{};
+  fa.rq = rq;
+  fa.rk = rk;
+  fa.dg = dg;
+  fa.chunk_r = (float*)(w + p.off_r);
+  fa.B = dims->B;
+  fa.T = dims->T;
+  fa.H = dims->H;
+  fa.n_chunks = p.n_chunks;
+  e = launch_bwd_finish(fa, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd finish");
+  e = launch_dg_finish(dg, fa.chunk_r, dS_T, S_T, dS0, g, dims->B, dims->T, dims->H, p.n_chunks, st);
+  return device_err(e, "gla_chunk_bwd dg finish");
+}
+
 }  // namespace
 
 extern "C" {
@@ -559,11 +723,31 @@ size_t gla_state_slot_bytes(int32_t H, int32_t dk, int32_t dv) {
 
 
 gla_status gla_state_alloc(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, void* stream, gla_state** out) {
-  return alloc_pool(n_slots, H, dk, dv, GLA_STATE_F32, stream, out);
+  return alloc_pool(n_slots, H, dk, dv, GLA_STATE_F32, 0, stream, out);
 }
 
 gla_status gla_state_alloc_q16(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, void* stream, gla_state** out) {
-  return alloc_pool(n_slots, H, dk, dv, GLA_STATE_Q16, stream, out);
+  return alloc_pool(n_slots, H, dk, dv, GLA_STATE_Q16, 0, stream, out);
+}
+
+gla_status gla_state_alloc_conv(int64_t n_slots, int32_t H, int32_t dk, int32_t dv, int32_t format, int32_t conv_D,
+                                void* stream, gla_state** out) {
+  if (!out) return fail(GLA_ERR_INVALID_ARGUMENT, "out must not be NULL");
+  *out = nullptr;
+  TRY(check_conv_D(conv_D));
+  return alloc_pool(n_slots, H, dk, dv, format, conv_D, stream, out);
+}
+
+int32_t gla_state_conv_channels(const gla_state* pool) { return pool ? pool->conv_D : 0; }
+
+float* gla_state_conv_ptr(const gla_state* pool, int64_t slot) {
+  if (!pool || !pool->conv || slot < 0 || slot >= pool->n_slots) return nullptr;
+  return pool->conv + slot * (int64_t)CONV_WIN * pool->conv_D;
+}
+
+size_t gla_state_seq_bytes(int32_t H, int32_t dk, int32_t dv, int32_t format, int32_t conv_D) {
+  if (H < 1 || dk < 1 || dv < 1 || conv_D < 0 || (format != GLA_STATE_F32 && format != GLA_STATE_Q16)) return 0;
+  return slot_bytes(H, dk, dv, format, conv_D);
 }
 
 int32_t gla_state_format(const gla_state* pool) { return pool ? pool->format : -1; }
@@ -614,9 +798,12 @@ gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes) {
     return ok();
   }
   if (op == GLA_OP_BWD) {
-    if (dims->in_dtype != GLA_BF16)
-      return fail(GLA_ERR_UNSUPPORTED, "the backward is implemented for bf16 inputs only");
-    *bytes = plan_bwd(dims).ws_total;
+    if (dims->in_dtype == GLA_F32) {
+      TRY(check_bwd_f32_plan(dims));
+      *bytes = plan_bwd_f32(dims).ws_total;
+    } else {
+      *bytes = plan_bwd(dims).ws_total;
+    }
     return ok();
   }
   if (op == GLA_OP_FWD_VARLEN_Q16) {
@@ -655,8 +842,9 @@ gla_status gla_chunk_fwd_noalloc(const gla_dims* dims, const void* q, const void
 
 gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q, const gla_strides* sq, const void* k,
                                  const gla_strides* sk, const void* v, const gla_strides* sv, const float* g,
-                                 const gla_strides* sg, const float* S0, void* o, const gla_strides* so,
-                                 float* S_T, void* ws, size_t ws_bytes, void* stream) {
+                                 const gla_strides* sg, const void* gate, const gla_strides* sgate,
+                                 const float* S0, void* o, const gla_strides* so, float* S_T, void* ws,
+                                 size_t ws_bytes, void* stream) {
   TRY(check_dims(dims));
   TRY(check_ptr(q, "q", false));
   TRY(check_ptr(k, "k", false));
@@ -671,6 +859,9 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q, const gla_
   TRY(check_strides(sv, isz, true, "v"));
   TRY(check_strides(so, osz, true, "o"));
   TRY(check_strides(sg, 4, false, "g"));
+  TRY(check_ptr(gate, "gate", true));
+  if (!gate && sgate) return fail(GLA_ERR_INVALID_ARGUMENT, "gate strides given without a gate");
+  TRY(check_strides(sgate, isz, true, "gate"));
   const FwdPlan p = plan_fwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   if (p.ws_total > 0) TRY(check_ptr(ws, "ws", false));
@@ -684,6 +875,7 @@ gla_status gla_chunk_fwd_strided(const gla_dims* dims, const void* q, const gla_
   if (sk) a.X = strided_view(k, *sk, 0);
   if (sv) a.Y = strided_view(v, *sv, w);
   if (so) a.O = strided_view(o, *so, w);
+  if (gate) a.G = sgate ? strided_view(gate, *sgate, w) : tok_view(gate, isz, dims, DV, w, false);
   if (sg) {
     a.gsb = sg->batch;
     a.gst = sg->token;
@@ -799,14 +991,17 @@ gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv, int3
                     "gla_recurrent_step launch");
 }
 
-gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, int32_t out_dtype,
-                           const int32_t* cu_seqlens, int64_t total_tokens, const void* x, const float* w,
-                           const float* bias, void* conv_state, const int32_t* slot_idx, int32_t init_from_state,
-                           void* y, void* stream) {
+namespace {
+
+// The convolution over [B,T,D] or packed rows, with the window rows of
+// `window` ([slots][4][D] float32, or null) addressed through slot_idx.
+gla_status conv_call(int64_t B, int64_t T, int32_t D, int32_t in_dtype, int32_t out_dtype, const int32_t* cu_seqlens,
+                     int64_t total_tokens, const void* x, const float* w, const float* bias, float* window,
+                     int64_t n_slots, const int32_t* slot_idx, int32_t init, void* y, void* stream,
+                     const char* name) {
   if (B < 1 || T < 1) return fail(GLA_ERR_INVALID_ARGUMENT, "B and T must be >= 1 (got B=%lld, T=%lld)",
                                   (long long)B, (long long)T);
-  if (D < 8 || D % 8 != 0 || D > (1 << 16))
-    return fail(GLA_ERR_UNSUPPORTED, "D must be a multiple of 8 in [8, 65536] (got %d)", D);
+  TRY(check_conv_D(D));
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return fail(GLA_ERR_INVALID_ARGUMENT, "in_dtype/out_dtype must be GLA_F32 or GLA_BF16");
   if (cu_seqlens) {
@@ -817,45 +1012,65 @@ gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, in
     return fail(GLA_ERR_UNSUPPORTED, "B*T too large");
   }
   if (B > ((int64_t)1 << 36) / (T * (D / 8))) return fail(GLA_ERR_UNSUPPORTED, "B*T*D too large");
-  if (init_from_state != 0 && init_from_state != 1)
-    return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_state must be 0 or 1 (got %d)", init_from_state);
-  if (init_from_state && !conv_state)
-    return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_state needs conv_state");
+  if (init != 0 && init != 1) return fail(GLA_ERR_INVALID_ARGUMENT, "%s: the init flag must be 0 or 1 (got %d)", name, init);
   TRY(check_ptr(x, "x", false));
   TRY(check_ptr(w, "w", false));
   TRY(check_ptr(bias, "bias", true));
-  TRY(check_ptr(conv_state, "conv_state", true));
   if (slot_idx && ((uintptr_t)slot_idx & 3u)) return fail(GLA_ERR_INVALID_ARGUMENT, "slot_idx must be 4-byte aligned");
   TRY(check_ptr(y, "y", false));
-  // the history tensor is the caller's: its slot count is unknown here, so
-  // only negative and repeated indices are caught
-  TRY(debug_checks((hipStream_t)stream, "gla_conv1d_silu", [&](int* f) {
+  TRY(debug_checks((hipStream_t)stream, name, [&](int* f) {
     hipError_t e_ = cu_seqlens ? debug_offsets(cu_seqlens, B, total_tokens, T, f, (hipStream_t)stream) : hipSuccess;
-    if (e_ == hipSuccess && conv_state) e_ = debug_slots(slot_idx, B, INT64_MAX, f, (hipStream_t)stream);
+    if (e_ == hipSuccess && window) e_ = debug_slots(slot_idx, B, n_slots, f, (hipStream_t)stream);
     return e_;
   }));
   ConvArgs a{};
   a.x = x;
   a.w = w;
   a.bias = bias;
-  a.state = conv_state;
+  a.state = window;
   a.slot = slot_idx;
   a.cu = cu_seqlens;
   a.B = B;
   a.T = T;
   a.total = cu_seqlens ? total_tokens : B * T;
   a.D = D;
-  a.init = init_from_state;
+  a.init = init;
   a.y = y;
-  return device_err(launch_conv(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream),
-                    "gla_conv1d_silu launch");
+  return device_err(launch_conv(a, in_dtype == GLA_BF16, out_dtype == GLA_BF16, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+gla_status gla_conv1d_silu(int64_t B, int64_t T, int32_t D, int32_t in_dtype, int32_t out_dtype,
+                           const int32_t* cu_seqlens, int64_t total_tokens, const void* x, const float* w,
+                           const float* bias, float* conv_state, const int32_t* slot_idx, int32_t init_from_state,
+                           void* y, void* stream) {
+  if (init_from_state && !conv_state)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "init_from_state needs conv_state");
+  TRY(check_ptr(conv_state, "conv_state", true));
+  // the window tensor is the caller's: its slot count is unknown here, so
+  // only negative and repeated indices are caught under GLA_DEBUG
+  return conv_call(B, T, D, in_dtype, out_dtype, cu_seqlens, total_tokens, x, w, bias, conv_state, INT64_MAX,
+                   slot_idx, init_from_state, y, stream, "gla_conv1d_silu");
+}
+
+gla_status gla_conv1d_silu_pool(int64_t B, int64_t T, int32_t in_dtype, int32_t out_dtype, const int32_t* cu_seqlens,
+                                int64_t total_tokens, const void* x, const float* w, const float* bias,
+                                gla_state* pool, const int32_t* slot_idx, int32_t init_from_pool, void* y,
+                                void* stream) {
+  if (!pool) return fail(GLA_ERR_INVALID_ARGUMENT, "pool must not be NULL");
+  if (!pool->conv) return fail(GLA_ERR_INVALID_ARGUMENT, "the pool has no convolution window (gla_state_alloc_conv)");
+  if (!slot_idx && B > pool->n_slots)
+    return fail(GLA_ERR_INVALID_ARGUMENT, "B=%lld sequences exceed the pool's %lld slots", (long long)B,
+                (long long)pool->n_slots);
+  return conv_call(B, T, pool->conv_D, in_dtype, out_dtype, cu_seqlens, total_tokens, x, w, bias, pool->conv,
+                   pool->n_slots, slot_idx, init_from_pool, y, stream, "gla_conv1d_silu_pool");
 }
 
 gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
                          const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dv, float* dg,
                          float* dS0, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_dims(dims));
-  if (dims->in_dtype != GLA_BF16) return fail(GLA_ERR_UNSUPPORTED, "the backward is implemented for bf16 inputs only");
   TRY(check_ptr(q, "q", false));
   TRY(check_ptr(k, "k", false));
   TRY(check_ptr(v, "v", false));
@@ -868,6 +1083,7 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   TRY(check_ptr(dv, "dv", false));
   TRY(check_ptr(dg, "dg", false));
   TRY(check_ptr(dS0, "dS0", true));
+  if (dims->in_dtype == GLA_F32) return bwd_f32(dims, q, k, v, g, S0, dO, dS_T, dq, dk, dv, dg, dS0, ws, ws_bytes, stream);
   const BwdPlan p = plan_bwd(dims);
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   TRY(check_ptr(ws, "ws", false));

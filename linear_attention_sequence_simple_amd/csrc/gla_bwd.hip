@@ -113,6 +113,44 @@ __global__ void __launch_bounds__(256) dg_carry_kernel(float* dg, const float* c
   }
 }
 
+// The fp32 backward's dot products rq_t = q_t.dq_t and rk_t = k_t.dk_t from
+// the float32 gradients (the walks' own sums), and, for bf16 outputs, those
+// gradients rounded into the outputs.  32 lanes per (batch, token, head) row,
+// three of its 96 columns each, so that a wave reads two whole rows.
+__global__ void __launch_bounds__(256) row_dots_kernel(RowDotsArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= a.rows) return;
+  const int l = threadIdx.x & 31;
+  const int64_t off = row * DK + 3 * l;
+  float rq = 0.f, rk = 0.f;
+#pragma unroll
+  for (int e = 0; e < 3; ++e) {
+    rq += a.q[off + e] * a.dq[off + e];
+    rk += a.k[off + e] * a.dk[off + e];
+  }
+#pragma unroll
+  for (int m = 16; m > 0; m >>= 1) {
+    rq += __shfl_xor(rq, m, 32);
+    rk += __shfl_xor(rk, m, 32);
+  }
+  if (l == 0) {
+    a.rq[row] = rq;
+    a.rk[row] = rk;
+  }
+  if (a.dq_bf16) {
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      a.dq_bf16[off + e] = (bf16)a.dq[off + e];
+      a.dk_bf16[off + e] = (bf16)a.dk[off + e];
+    }
+  }
+}
+
+hipError_t launch_row_dots(const RowDotsArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(row_dots_kernel, dim3((unsigned)((a.rows + 7) / 8)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_finish(const BwdFinishArgs& a, hipStream_t st) {
   const int64_t items = a.B * a.H * a.n_chunks;
   hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);

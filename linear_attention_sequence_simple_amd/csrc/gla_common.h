@@ -275,6 +275,10 @@ __device__ __forceinline__ f32x4 load4f(const bf16* p) {
   return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
 
+// x * silu(a) = x * a / (1 + e^-a): the output gate (e^-a overflows to inf
+// for a below about -88, which gives -0).
+__device__ __forceinline__ float gate_silu(float x, float a) { return x * (a / (1.0f + __expf(-a))); }
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int l = lane_id();

@@ -6,8 +6,9 @@
 // ("Cómo i14 llevó Laplace 3B a AWS Trainium2", section "Diseño esencial de
 // Laplace 3B"):
 //     a_t[c] = bias[c] + sum_{j<4} w[c][j] x_{t-3+j}[c],   y_t[c] = a_t[c] / (1 + e^{-a_t[c]})
-// Tokens before a sequence's first come from its history (the last three
-// inputs of the previous call, kept per pool slot) or are zero.
+// Tokens before a sequence's first come from its window (the last four
+// inputs of the previous call, float32, kept per pool slot; the newest three
+// are read) or are zero.
 //
 // Plain streaming work: 2 bytes read and 2 written per bf16 token-channel, 9
 // flops.  Each thread owns 8 channels (one 16-byte piece of a bf16 row) of a
@@ -19,7 +20,7 @@
 // i + 8 is requested as token i is used.  Measured at 0.87 of a plain device
 // copy of the same tensors (about 4.6 against 5.2 TB/s).  The thread
 // of a sequence's first run (per 8 channels) is the only reader of its old
-// history, so it also writes the new one, after reading the old.
+// window, so it also writes the new one, after reading the old.
 #include "gla_common.h"
 #include "gla_kernels.h"
 
@@ -186,24 +187,28 @@ __global__ void __launch_bounds__(256) conv_kernel(ConvArgs a) {
   const int c0 = 8 * cg;
   const int64_t D = a.D;
   const TIn* xs = (const TIn*)a.x + t0 * D + c0;
-  TIn* hist = a.state ? (TIn*)a.state + (a.slot ? (int64_t)a.slot[b] : b) * 3 * D + c0 : nullptr;
-  const bool keeper = run == 0 && hist;        // writes the sequence's new history
+  float* hist = a.state ? a.state + (a.slot ? (int64_t)a.slot[b] : b) * CONV_WIN * D + c0 : nullptr;
+  const bool keeper = run == 0 && hist;        // writes the sequence's new window
   if (tb >= L && !keeper) return;
   // x_{tb-3}, x_{tb-2}, x_{tb-1}: earlier tokens of the sequence, else its
-  // history row t + 3, else zero
+  // window row t + 4 (row m holds x_{m-4}), else zero
   auto before = [&](int64_t t) {
-    return t >= 0 ? load8(xs + t * D) : (hist && a.init) ? load8(hist + (t + 3) * D) : zero8();
+    return t >= 0 ? load8(xs + t * D) : (hist && a.init) ? load8(hist + (t + CONV_WIN) * D) : zero8();
   };
   Window h{before(tb - 3), before(tb - 2), before(tb - 1)};
-  if (keeper) {
-    // rows L, L+1, L+2 of (old history, tokens): for L < 3 partly the old
-    // rows, which h holds (tb = 0); every source is read before the writes
-    const Row8 n0 = L >= 3 ? load8(xs + (L - 3) * D) : L == 0 ? h.r0 : L == 1 ? h.r1 : h.r2;
-    const Row8 n1 = L >= 2 ? load8(xs + (L - 2) * D) : L == 0 ? h.r1 : h.r2;
-    const Row8 n2 = L >= 1 ? load8(xs + (L - 1) * D) : h.r2;
+  if (keeper && !(L == 0 && a.init)) {
+    // rows L..L+3 of (old window, tokens), with h holding old rows 1..3 (or
+    // zeros without init) since tb = 0; row 0 of the old window is needed
+    // only when L = 0, where the window stays as it is (with init) or is the
+    // zero window (without).  Every source is read before the writes.
+    const Row8 n0 = L >= 4 ? load8(xs + (L - 4) * D) : L == 3 ? h.r2 : L == 2 ? h.r1 : L == 1 ? h.r0 : zero8();
+    const Row8 n1 = L >= 3 ? load8(xs + (L - 3) * D) : L == 2 ? h.r2 : L == 1 ? h.r1 : h.r0;
+    const Row8 n2 = L >= 2 ? load8(xs + (L - 2) * D) : L == 1 ? h.r2 : h.r1;
+    const Row8 n3 = L >= 1 ? load8(xs + (L - 1) * D) : h.r2;
     store8(hist, n0);
     store8(hist + D, n1);
     store8(hist + 2 * D, n2);
+    store8(hist + 3 * D, n3);
   }
   if (tb < L) conv_tokens<TIn, TOut>(a, c0, xs, (TOut*)a.y + t0 * D + c0, tb, (int)min((int64_t)CONV_RUN, L - tb), h);
 }

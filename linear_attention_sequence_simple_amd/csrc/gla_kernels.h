@@ -18,6 +18,9 @@ enum WalkVariant {
   WV_FWD_OUT_F32_BF16 = 3,
   WV_FWD_STATE_BF16 = 4,
   WV_FWD_STATE_F32 = 5,
+  // fp32 in and out, 32-column value slices (three over a 96-wide value
+  // tile): the fp32 backward's walks whose values are k or q
+  WV_OUT_F32_NC1 = 6,
 };
 
 // A token tensor as one walk sees it: column j of dv-slice s of token t (in
@@ -45,10 +48,13 @@ struct WalkArgs {
   TokView Y;            // values          (width 96 per slice; 64 for fp32 inputs)
   TokView Q;            // queries         (width 96), with output only
   TokView O;            // outputs         (width of Y), with output only
+  TokView G;            // with output: gate in the input dtype, same columns as O
+                        // (p null: none); o_t <- o_t * silu(gate_t) before the store
   const float* g;       // log-decay of walk token t: g[b*gsb + h*gsh + (t - gshift)*gst],
   int64_t gsb, gsh, gst;  // zero for t < gshift
   int gshift;
-  TokView acc;          // with output: fp32 partial sums added to the outputs (p null: none)
+  TokView acc;          // with output: fp32 partial sums added to the outputs (p null: none),
+                        // the layout of O (fp32)
   TokView D;            // with acc: rows dotted with the final outputs (bf16, width of Y)
   TokView rdot;         // with acc: those dot products, one float per token (p null: none)
   StateView zinit;      // initial state (p null: zero)
@@ -85,12 +91,14 @@ hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, cons
 // Decode step: see gla_step.hip.
 // The convolution ahead of the mixer (gla_conv.hip): sequence b is rows
 // cu[b]..cu[b+1] of x (cu null: rows b*T..(b+1)*T), at most T tokens; its
-// history (when state is set) is rows [3] of slot slot[b] (slot null: b).
+// window (when state is set) is the CONV_WIN rows of slot slot[b] (slot
+// null: b), row m holding x_{m-4}.
+constexpr int CONV_WIN = 4;
 struct ConvArgs {
   const void* x;
   const float* w;       // [D, 4]
   const float* bias;    // [D] or null
-  void* state;          // [slots, 3, D] in the input dtype, or null
+  float* state;         // [slots, CONV_WIN, D] float32, or null
   const int32_t* slot;
   const int32_t* cu;
   int64_t B, T, total;
@@ -135,6 +143,16 @@ struct BwdFinishArgs {
   int64_t B, T; int H, n_chunks;
 };
 hipError_t launch_bwd_finish(const BwdFinishArgs& a, hipStream_t st);
+// fp32 backward: rq = q.dq and rk = k.dk per [B,T,H] row from float32
+// q, k, dq, dk ([rows][DK]); with dq_bf16 set, dq and dk rounded into
+// dq_bf16 and dk_bf16.
+struct RowDotsArgs {
+  const float* q; const float* k; const float* dq; const float* dk;
+  float* rq; float* rk;
+  __bf16* dq_bf16; __bf16* dk_bf16;
+  int64_t rows;
+};
+hipError_t launch_row_dots(const RowDotsArgs& a, hipStream_t st);
 hipError_t launch_dg_finish(float* dg, const float* chunk_r, const float* dS_T, const float* S_T, float* dS0,
                             const float* g, int64_t B, int64_t T, int H, int n_chunks, hipStream_t st);
 

@@ -53,9 +53,11 @@ struct Own {
       // second active wave to overlap the output wave's stalls
       if (NC == 3) return u < 2 ? 3 : u == 2 ? 2 : 1;
       if (NC == 2) return u == 0 ? 3 : u == 1 ? 2 : u == 2 ? 1 : 0;
+      if (NC == 1) return u < 3 ? 1 : 0;
     } else {
       if (NC == 3) return u == 0 ? 3 : 2;
       if (NC == 2) return u < 2 ? 2 : 1;
+      if (NC == 1) return u < 3 ? 1 : 0;
     }
     return 0;
   }
@@ -204,7 +206,7 @@ __device__ __forceinline__ int64_t state_row(const int32_t* idx, int b, int h, i
   return (int64_t)b * H + h;
 }
 
-template <class TIn, class TOut, int NC, int MODE, int W, bool PACKED>
+template <class TIn, class TOut, int NC, int MODE, int W, bool PACKED, bool GATED>
 __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm,
                                           int b, int h, int slice, int seg) {
   constexpr bool OUT = MODE == WALK_FWD_OUT;
@@ -402,6 +404,33 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
           for (int cb = 0; cb < NC; ++cb)
             o[cb] = mfma(frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s), pf[J][s], o[cb]);
       const int64_t trow = (int64_t)n * CH + il;
+      if (a.acc.p && trow < T) {
+        // add a partial sum of the same outputs (fp32, computed by another
+        // walk over the other half of a contraction)
+        const float* ap = (const float*)a.acc.p + b * a.acc.sb + sq.t0 * a.acc.st + h * a.acc.sh + trow * a.acc.st +
+                          slice * a.acc.ss + 4 * g2;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 v = load4f(ap + 32 * cb + 8 * qq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] += v[e];
+          }
+      }
+      if (GATED && trow < T) {
+        // output gate: this lane's token row, the same columns as its outputs
+        const TIn* gp = (const TIn*)a.G.p + b * a.G.sb + sq.t0 * a.G.st + h * a.G.sh + trow * a.G.st +
+                        slice * a.G.ss + 4 * g2;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 gv = load4f(gp + 32 * cb + 8 * qq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] = gate_silu(o[cb][4 * qq + e], gv[e]);
+          }
+      }
       if (trow < T) {
         TOut* op = (TOut*)a.O.p + b * a.O.sb + sq.t0 * a.O.st + h * a.O.sh + trow * a.O.st + slice * a.O.ss + 4 * g2;
 #pragma unroll
@@ -530,7 +559,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 // overlaps the products.  All tiles are read from memory with row-contiguous
 // 16-byte accesses, spread over both phases so that the workgroups on the
 // chip keep the memory busy instead of all loading at the same moment.
-template <class TOut, int W, bool PACKED>
+template <class TOut, int W, bool PACKED, bool GATED>
 __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3, true>& sm, int b, int h,
                                              int slice, int seg) {
   using S = WalkSmem<bf16, 3, true>;
@@ -761,14 +790,28 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
 
     // ================= phase 2
     if constexpr (OUTW) {
-      // O^T += V^T P^T
+      // O^T += V^T P^T.  A gated walk requests this lane's gate (its token
+      // row, the same columns as its outputs) before the last key block's
+      // products, once the earlier blocks' P operands are dead (requested
+      // earlier, the gate's registers spill).
       constexpr int NK = 2 * (W + 1);                   // (J, s) steps
       bf16x8 yv[2][NC];
+      bf16x4 gt[GATED ? NC : 1][4];
+      const int64_t grow = (int64_t)n * CH + 32 * W + (lane & 31);
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) yv[0][cb] = sfrag_kr(sm.y, 0, 32 * cb, 0);
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
         const int bf = k & 1, J = k >> 1, s = k & 1;
+        if (GATED && k == NK - 2) {
+          const bool live = grow < T;
+          const bf16* gp = (const bf16*)a.G.p + b * a.G.sb + sq.t0 * a.G.st + h * a.G.sh +
+                           (live ? grow : 0) * a.G.st + slice * a.G.ss + 4 * g2;
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) gt[cb][qq] = live ? *(const bf16x4*)(gp + 32 * cb + 8 * qq) : bf16x4{};
+        }
         if (k + 1 < NK) {
 #pragma unroll
           for (int cb = 0; cb < NC; ++cb) yv[bf ^ 1][cb] = sfrag_kr(sm.y, 32 * ((k + 1) >> 1), 32 * cb, (k + 1) & 1);
@@ -809,6 +852,14 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
           if (g2 == 0 && live)
             ((float*)a.rdot.p)[b * a.rdot.sb + (sq.t0 + trow) * a.rdot.st + h * a.rdot.sh] = r;
         }
+      }
+      if constexpr (GATED) {
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] = gate_silu(o[cb][4 * qq + e], (float)gt[cb][qq][e]);
       }
       if constexpr (std::is_same<TOut, bf16>::value) {
         // Through this wave's own rows of the query tile (free until the
@@ -929,7 +980,7 @@ __device__ __forceinline__ int longest_first(const WalkArgs& a, int i) {
 }
 
 // The walk of workgroup `local` of a launch of `nwg` workgroups.
-template <class TIn, class TOut, int NC, int MODE, bool PACKED = false>
+template <class TIn, class TOut, int NC, int MODE, bool PACKED = false, bool GATED = false>
 __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm, int local,
                                            int nwg) {
   // Work item order: slice fastest, then segment, head, batch.  Equal-length
@@ -956,29 +1007,29 @@ __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, 
   if constexpr (PACKED) b = longest_first(a, b);
   if constexpr (MODE == WALK_FWD_OUT && std::is_same<TIn, bf16>::value) {
     switch (threadIdx.x >> 6) {
-      case 0: prefill_wave<TOut, 0, PACKED>(a, sm, b, h, slice, seg); break;
-      case 1: prefill_wave<TOut, 1, PACKED>(a, sm, b, h, slice, seg); break;
-      case 2: prefill_wave<TOut, 2, PACKED>(a, sm, b, h, slice, seg); break;
-      case 3: prefill_wave<TOut, 3, PACKED>(a, sm, b, h, slice, seg); break;
-      case 4: prefill_wave<TOut, 4, PACKED>(a, sm, b, h, slice, seg); break;
-      case 5: prefill_wave<TOut, 5, PACKED>(a, sm, b, h, slice, seg); break;
-      case 6: prefill_wave<TOut, 6, PACKED>(a, sm, b, h, slice, seg); break;
-      default: prefill_wave<TOut, 7, PACKED>(a, sm, b, h, slice, seg); break;
+      case 0: prefill_wave<TOut, 0, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 1: prefill_wave<TOut, 1, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 2: prefill_wave<TOut, 2, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 3: prefill_wave<TOut, 3, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 4: prefill_wave<TOut, 4, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 5: prefill_wave<TOut, 5, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 6: prefill_wave<TOut, 6, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      default: prefill_wave<TOut, 7, PACKED, GATED>(a, sm, b, h, slice, seg); break;
     }
     return;
   } else {
   switch (threadIdx.x >> 6) {
-    case 0: walk_wave<TIn, TOut, NC, MODE, 0, PACKED>(a, sm, b, h, slice, seg); break;
-    case 1: walk_wave<TIn, TOut, NC, MODE, 1, PACKED>(a, sm, b, h, slice, seg); break;
-    case 2: walk_wave<TIn, TOut, NC, MODE, 2, PACKED>(a, sm, b, h, slice, seg); break;
-    case 3: walk_wave<TIn, TOut, NC, MODE, 3, PACKED>(a, sm, b, h, slice, seg); break;
+    case 0: walk_wave<TIn, TOut, NC, MODE, 0, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+    case 1: walk_wave<TIn, TOut, NC, MODE, 1, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+    case 2: walk_wave<TIn, TOut, NC, MODE, 2, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+    case 3: walk_wave<TIn, TOut, NC, MODE, 3, PACKED, GATED>(a, sm, b, h, slice, seg); break;
     default:
       if constexpr (WalkShape<MODE>::WAVES == 8) {
         switch (threadIdx.x >> 6) {
-          case 4: walk_wave<TIn, TOut, NC, MODE, 4, PACKED>(a, sm, b, h, slice, seg); break;
-          case 5: walk_wave<TIn, TOut, NC, MODE, 5, PACKED>(a, sm, b, h, slice, seg); break;
-          case 6: walk_wave<TIn, TOut, NC, MODE, 6, PACKED>(a, sm, b, h, slice, seg); break;
-          default: walk_wave<TIn, TOut, NC, MODE, 7, PACKED>(a, sm, b, h, slice, seg); break;
+          case 4: walk_wave<TIn, TOut, NC, MODE, 4, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+          case 5: walk_wave<TIn, TOut, NC, MODE, 5, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+          case 6: walk_wave<TIn, TOut, NC, MODE, 6, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+          default: walk_wave<TIn, TOut, NC, MODE, 7, PACKED, GATED>(a, sm, b, h, slice, seg); break;
         }
       }
       break;
@@ -992,10 +1043,10 @@ __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, 
 template <class TIn, int MODE>
 constexpr int walk_waves_per_eu() { return (MODE == WALK_FWD_STATE && sizeof(TIn) == 2) ? 2 : 1; }
 
-template <class TIn, class TOut, int NC, int MODE, bool PACKED>
+template <class TIn, class TOut, int NC, int MODE, bool PACKED, bool GATED>
 __global__ void __launch_bounds__(WalkShape<MODE>::THREADS, (walk_waves_per_eu<TIn, MODE>())) walk_kernel(WalkArgs a) {
   __shared__ WalkSmem<TIn, NC, MODE == WALK_FWD_OUT> sm;
-  walk_block<TIn, TOut, NC, MODE, PACKED>(a, sm, (int)blockIdx.x, (int)gridDim.x);
+  walk_block<TIn, TOut, NC, MODE, PACKED, GATED>(a, sm, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Two independent state walks of one kind side by side: workgroups [0, nwg0)
@@ -1051,12 +1102,23 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(float* buf, const float* 
 }
 
 // ---------------------------------------------------------------------------
+// Packed walks and walks with an output gate are compile-time variants, so
+// that the plain walks keep their registers.
 template <class TIn, class TOut, int NC, int MODE>
 static hipError_t launch_one(const WalkArgs& a, int nwg, hipStream_t st) {
+  const dim3 grid(nwg), block(WalkShape<MODE>::THREADS);
+  if (a.cu && a.G.p) return hipErrorInvalidValue;        // not a combination the library launches
+  if constexpr (NC == 1) {                               // the fp32 backward's walks: plain views only
+    if (a.cu || a.G.p) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, false, false>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (a.cu)
-    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, true>), dim3(nwg), dim3(WalkShape<MODE>::THREADS), 0, st, a);
+    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, true, false>), grid, block, 0, st, a);
+  else if (MODE == WALK_FWD_OUT && a.G.p)
+    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, false, MODE == WALK_FWD_OUT>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, false>), dim3(nwg), dim3(WalkShape<MODE>::THREADS), 0, st, a);
+    hipLaunchKernelGGL((walk_kernel<TIn, TOut, NC, MODE, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -1068,6 +1130,7 @@ hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st) 
     case WV_FWD_OUT_F32_BF16: return launch_one<float, bf16, 2, WALK_FWD_OUT>(a, nwg, st);
     case WV_FWD_STATE_BF16: return launch_one<bf16, float, 3, WALK_FWD_STATE>(a, nwg, st);
     case WV_FWD_STATE_F32: return launch_one<float, float, 2, WALK_FWD_STATE>(a, nwg, st);
+    case WV_OUT_F32_NC1: return launch_one<float, float, 1, WALK_FWD_OUT>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1099,6 +1162,7 @@ hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& 
 int walk_slices(int variant) {
   switch (variant) {
     case WV_FWD_OUT_F32_F32: case WV_FWD_OUT_F32_BF16: case WV_FWD_STATE_F32: return DV / 64;
+    case WV_OUT_F32_NC1: return DK / 32;
     default: return DV / 96;
   }
 }

@@ -29,13 +29,16 @@ pool slot's state ("AWS serve Laplace 3B di i14 con uno stato fisso di 29,5
 MB", sections "Lo stato di Laplace 3B resta fisso durante l'inferenza" and
 "I risultati dichiarati hanno limiti precisi"), and conv1d_silu is the causal
 depth-wise convolution of width 4 with SiLU that precedes the mixer ("Diseño
-esencial de Laplace 3B").  q16_encode, q16_decode and step_q16 hold the
+esencial de Laplace 3B"), and gate_silu (with forward_gated) is the output
+gate of the fused projection applied to the mixer's output (same section; the
+formula is a reading, see its docstring).  q16_encode, q16_decode and step_q16 hold the
 decode state in 16 bits (an int16 mantissa per element, one power-of-two
 exponent per state column), after the INT16 storage of the HEAL summary
 (section "A. Mitigando o Truncamento de Atenção via Quantização INT16").
 Every function is pinned by tests that do not reuse its formula:
-tests/test_oracle.py, tests/test_oracle_packed.py, tests/test_oracle_conv.py
-and tests/test_oracle_q16.py with the fixtures under tests/golden/.
+tests/test_oracle.py, tests/test_oracle_packed.py, tests/test_oracle_conv.py,
+tests/test_oracle_q16.py and tests/test_oracle_gate.py with the fixtures
+under tests/golden/.
 
 Everything is float64.  Inputs may be any float dtype; callers pass the exact
 values the device sees (bf16 inputs already rounded to bf16).
@@ -48,7 +51,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "forward_packed", "step", "backward", "conv1d_silu", "state_bytes",
+__all__ = ["forward", "forward_packed", "step", "backward", "conv1d_silu", "state_bytes", "gate_silu", "forward_gated",
            "q16_encode", "q16_decode", "step_q16", "Q16_MAX", "Q16_NAN"]
 
 
@@ -195,13 +198,20 @@ def conv1d_silu(x, w, bias, cu_seqlens, state=None, slot_idx=None, init_from_sta
         y_t[c] = a_t[c] / (1 + exp(-a_t[c]))           (SiLU)
 
     so w[c, 3] weights the current token.  Tokens before the sequence's first
-    come from its slot of `state` ([n_slots, 3, D], row m holding x_{m-3})
-    when init_from_state is set, else are zero.  x is [N, D] with sequence b
-    at rows cu_seqlens[b] to cu_seqlens[b+1]; w is [D, 4]; bias [D] or None.
+    come from its slot of `state` when init_from_state is set, else are zero.
+    A slot is the convolution's window of the last four inputs,
+    [n_slots, 4, D] with row m holding x_{m-4}: the width of the filter, the
+    form in which the per-sequence state reaches the 29.5 MB the pages print
+    (24 layers of a float32 mixer state and a float32 window of 4 x 3,072;
+    "Lo stato di Laplace 3B resta fisso durante l'inferenza").  Row 0, the
+    oldest, is not read by the next token; it is kept so that the window is
+    the filter's full width.  x is [N, D] with sequence b at rows
+    cu_seqlens[b] to cu_seqlens[b+1]; w is [D, 4]; bias [D] or None.
 
     Returns (y [N, D], new state or None) in float64: with a state, each
-    sequence's slot receives the last three inputs of its history followed by
-    its tokens; other slots keep theirs; the state passed in is not modified.
+    sequence's slot receives the last four rows of its window followed by its
+    tokens (the window of zeros when init_from_state is not set); other slots
+    keep theirs; the state passed in is not modified.
     """
     x, w = _f64(x), _f64(w)
     N, D = x.shape
@@ -214,15 +224,15 @@ def conv1d_silu(x, w, bias, cu_seqlens, state=None, slot_idx=None, init_from_sta
     new_state = None if state is None else state.copy()
     for b in range(n_seq):
         t0, t1 = cu[b], cu[b + 1]
-        hist = state[slots[b]] if (state is not None and init_from_state) else np.zeros((3, D))
-        z = np.concatenate([hist, x[t0:t1]], 0)        # z[m] = x_{m-3}
+        hist = state[slots[b]] if (state is not None and init_from_state) else np.zeros((4, D))
+        z = np.concatenate([hist, x[t0:t1]], 0)        # z[m] = x_{m-4}
         for t in range(t1 - t0):
             a = bias.copy()
             for j in range(4):
-                a += w[:, j] * z[t + j]
+                a += w[:, j] * z[t + 1 + j]             # x_{t-3+j}
             y[t0 + t] = a / (1.0 + np.exp(-a))
         if new_state is not None:
-            new_state[slots[b]] = z[-3:]
+            new_state[slots[b]] = z[-4:]
     return y, new_state
 
 
@@ -285,6 +295,30 @@ def step_q16(m, e, q, k, v, g):
     o, S = step(q16_decode(m, e), q, k, v, g)
     m_new, e_new = q16_encode(S)
     return o, m_new, e_new
+
+
+def gate_silu(o, gate):
+    """The output gate applied to the mixer's output: o_t * SiLU(gate_t).
+
+    The fused projection of "Diseño esencial de Laplace 3B" ("Cómo i14 llevó
+    Laplace 3B a AWS Trainium2") splits into q, k, v and a gate g_t, dv values
+    per head (9,216 = H(2dk + 2dv)); the pages do not print how the gate meets
+    the mixer's output.  The plainest reading: elementwise, through the one
+    activation that section names (SiLU, after the convolution),
+
+        y_t[h, c] = o_t[h, c] * gate_t[h, c] / (1 + exp(-gate_t[h, c]))
+
+    o and gate have the same shape ([..., dv]); returns y in float64.
+    """
+    o, gate = _f64(o), _f64(gate)
+    with np.errstate(over="ignore"):
+        return o * (gate / (1.0 + np.exp(-gate)))
+
+
+def forward_gated(q, k, v, g, gate, S0=None):
+    """`forward` followed by `gate_silu` on its output: (y, S_T)."""
+    o, S = forward(q, k, v, g, S0)
+    return gate_silu(o, gate), S
 
 
 def state_bytes(H, dk, dv, itemsize=4):

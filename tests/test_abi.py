@@ -58,8 +58,12 @@ def test_workspace_sizes(L):
     # fp32 sums of dq and dk over the first dv-half, and q.dq, k.dk per token
     tokens = 2 * 300 * 16
     assert n >= 2 * tokens * 96 * 4 + 2 * tokens * 4
-    st, _ = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32))
-    assert st == 2 and "bf16" in L.gla_last_error().decode()
+    # fp32 inputs: first-half sums, float32 gradients for bf16 outputs, dot
+    # products, the final state and chunk sums; whole sequences only
+    st, n32 = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32, out_dtype=gla.GLA_BF16))
+    assert st == 0 and n32 >= 4 * tokens * 96 * 4 + 2 * tokens * 4
+    st, _ = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32, segments=2))
+    assert st == 2 and "whole sequences" in L.gla_last_error().decode()
     st, _ = ws_size(L, 7, dims())
     assert st == 1
     # a packed prefill into a 16-bit pool stages one float32 state per
@@ -176,15 +180,18 @@ def test_strided_validation(L):
     p = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
     S = gla.GlaStrides
     dense_q = S(300 * 16 * 96, 16 * 96, 96)
-    call = lambda sq=None, sg=None, so=None, g=p: L.gla_chunk_fwd_strided(
-        ctypes.byref(d), p, sq and ctypes.byref(sq), p, None, p, None, g, sg and ctypes.byref(sg), None, p,
-        so and ctypes.byref(so), None, None, 0, None)
+    call = lambda sq=None, sg=None, so=None, g=p, gate=None, sgate=None: L.gla_chunk_fwd_strided(
+        ctypes.byref(d), p, sq and ctypes.byref(sq), p, None, p, None, g, sg and ctypes.byref(sg), gate,
+        sgate and ctypes.byref(sgate), None, p, so and ctypes.byref(so), None, None, 0, None)
     assert call(sq=S(0, 96, 96)) == 1 and "positive" in L.gla_last_error().decode()
     assert call(sq=S(9216 * 300, 9216, 100)) == 1 and "16 bytes" in L.gla_last_error().decode()
     assert call(sq=S(1 << 40, 1 << 30, 96)) == 1 and "too large" in L.gla_last_error().decode()
     assert call(so=S(-1, 192, 192)) == 1
     assert call(g=ctypes.c_void_p(0x10002)) == 1 and "g must be" in L.gla_last_error().decode()
     assert call(sq=dense_q, sg=S(300 * 17, 17, 0)) == 1 and "g strides" in L.gla_last_error().decode()
+    assert call(gate=ctypes.c_void_p(0x10008)) == 1 and "gate" in L.gla_last_error().decode()
+    assert call(sgate=S(9216 * 300, 9216, 576)) == 1 and "without a gate" in L.gla_last_error().decode()
+    assert call(gate=p, sgate=S(9216 * 300, 9216, 100)) == 1 and "gate strides" in L.gla_last_error().decode()
 
 
 def test_noalloc_scratch_limit(L):
@@ -221,3 +228,16 @@ def test_header_and_library_from_plain_c(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
+
+
+def test_page_sizes_of_the_library_slot(L):
+    """A slot of a pool made with a convolution window holds a layer's whole
+    per-sequence state; 24 of them are the printed 29.5 MB."""
+    import oracle
+    from conftest import read_golden
+    d = read_golden("page_sizes.txt")
+    H, dk, dv, D = int(d["H"]), int(d["dk"]), int(d["dv"]), int(d["D"])
+    per = L.gla_state_seq_bytes(H, dk, dv, gla.GLA_STATE_F32, D)
+    assert per == oracle.state_bytes(H, dk, dv) + d["conv_width"] * D * 4
+    assert abs(d["layers"] * per / 1e6 - d["state_mb_per_sequence"]) < 0.05
+    assert L.gla_state_seq_bytes(H, dk, dv, gla.GLA_STATE_F32, 0) == L.gla_state_slot_bytes(H, dk, dv)

@@ -110,3 +110,70 @@ def test_longest_supported_sequence():
     ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], d["S0"], d["dS_T"], ckpt=1024)
     for name, x, y in zip(("dq", "dk", "dv", "dg", "dS0"), got, ref):
         assert_close(x, y, TOL, name)
+
+
+# ---------------------------------------------------------------------------
+# fp32 inputs: the same gradients on the fp32 matrix cores, bound 1e-4
+
+TOL_F32 = 1e-4
+
+
+def run_bwd_f32(d, S0=True, dS_T=True, out_dtype=torch.float32):
+    import linear_attention_sequence_simple_amd as gla
+    r = gla.gla_chunk_bwd(to_dev(d["q"], torch.float32), to_dev(d["k"], torch.float32),
+                          to_dev(d["v"], torch.float32), to_dev(d["g"], torch.float32),
+                          to_dev(d["dO"], torch.float32),
+                          S0=to_dev(d["S0"], torch.float32) if S0 else None,
+                          dS_T=to_dev(d.get("dS_T"), torch.float32) if dS_T else None,
+                          out_dtype=out_dtype, want_dS0=True)
+    torch.cuda.synchronize()
+    return [to_np(x) for x in r]
+
+
+def check_f32(d, got, S0=True, dS_T=True, tol=TOL_F32):
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], d["S0"] if S0 else None,
+                          d.get("dS_T") if dS_T else None)
+    for name, x, y in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close(x, y, tol, name)
+    dg, dg_ref = got[3], ref[3]
+    if np.all(dg_ref == 0):
+        scale = np.sqrt(np.mean(np.einsum("bthd,bthd->bth", d["q"], ref[0]) ** 2))
+        assert np.max(np.abs(dg)) <= tol * scale
+    else:
+        assert_close(dg, dg_ref, tol, "dg")
+    if S0 or dS_T:
+        assert_close(got[4], ref[4], tol, "dS0")
+
+
+@pytest.mark.parametrize("T", [1, 77, 128, 300, 513])
+@pytest.mark.parametrize("s0,dst", [(True, True), (False, False), (False, True)])
+def test_f32_reduced(T, s0, dst):
+    d = inputs("fwd_f32_b1_t2048", seed=60 + T, B=2, T=T, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
+    print(f"case bwd fp32 T={T} S0={s0} dS_T={dst}", flush=True)
+    check_f32(d, run_bwd_f32(d, s0, dst), s0, dst)
+
+
+@pytest.mark.parametrize("g", ["one", "zero"])
+def test_f32_special_decays(g):
+    d = inputs("fwd_f32_b1_t2048", seed=70, B=1, T=260, H=2, g=g, S0="normal0.1", with_dO=True, with_dS_T=True)
+    print(f"case bwd fp32 g={g}", flush=True)
+    check_f32(d, run_bwd_f32(d))
+
+
+def test_f32_training_shape():
+    """B=1, H=16, T=2048 (the fp32 workload's shape), every gradient of every
+    head against the oracle."""
+    d = inputs("fwd_f32_b1_t2048", seed=71, with_dO=True, with_dS_T=True, S0="normal0.1")
+    print("case bwd fp32 B=1 T=2048 H=16", flush=True)
+    check_f32(d, run_bwd_f32(d))
+
+
+def test_f32_bf16_gradients():
+    d = inputs("fwd_f32_b1_t2048", seed=72, B=2, T=333, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
+    print("case bwd fp32 in, bf16 out", flush=True)
+    got = run_bwd_f32(d, out_dtype=torch.bfloat16)
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], d["S0"], d["dS_T"])
+    for name, x, y in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close_bf16_out(x, y, TOL_F32, name + "(bf16)")
+    assert_close(got[3], ref[3], TOL_F32, "dg")
+    assert_close(got[4], ref[4], TOL_F32, "dS0")

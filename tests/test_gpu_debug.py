@@ -69,7 +69,7 @@ def test_repeated_slots_rejected_before_any_kernel(gla, monkeypatch):
         gla.gla_state_write(pool, torch.zeros((3, 16, 96, 192), device=dev()), slots)
     torch.cuda.synchronize()
     assert torch.equal(pool.view(), before)          # no kernel touched the pool
-    hist = torch.zeros((4, 3, 64), dtype=torch.bfloat16, device=dev())
+    hist = torch.zeros((4, 4, 64), dtype=torch.float32, device=dev())
     x = torch.ones((3, 10, 64), dtype=torch.bfloat16, device=dev())
     w = torch.ones((64, 4), device=dev())
     with pytest.raises(gla.GlaError, match="repeated"):
@@ -78,6 +78,15 @@ def test_repeated_slots_rejected_before_any_kernel(gla, monkeypatch):
     torch.cuda.synchronize()
     assert not hist.any()
     pool.free()
+    # a pool's windows: the pool knows its slot count, so an index past it is caught too
+    cpool = gla.gla_state_alloc_conv(4, 64, H=2)
+    for bad, what in (([1, 2, 1], "repeated"), ([0, 4, 1], "out of range")):
+        with pytest.raises(gla.GlaError, match=what):
+            gla.gla_conv1d_silu_pool(x, w, cpool, slot_idx=torch.tensor(bad, dtype=torch.int32, device=dev()),
+                                     init_from_pool=True)
+    torch.cuda.synchronize()
+    assert not cpool.conv_view().any() and not cpool.view().any()
+    cpool.free()
 
 
 def test_bad_decay_rejected(gla, monkeypatch):

@@ -208,12 +208,11 @@ def test_conv_sweep(c):
     x = r.standard_normal((N, D)).astype(np.float32)
     w = (r.standard_normal((D, 4)) * 0.5).astype(np.float32)
     bias = (r.standard_normal(D) * 0.1).astype(np.float32)
-    state = r.standard_normal((B + 2, 3, D)).astype(np.float32) if c["hist"] else None
+    state = r.standard_normal((B + 2, 4, D)).astype(np.float32) if c["hist"] else None
     if c["in_dt"] == "bf16":
         x = gen.bf16_round(x)
-        state = None if state is None else gen.bf16_round(state)
     slots = r.permutation(B + 2)[:B].astype(np.int32) if c["hist"] else None
-    st = to_dev(state, TDT[c["in_dt"]]) if c["hist"] else None
+    st = to_dev(state, torch.float32) if c["hist"] else None
     xin = to_dev(x, TDT[c["in_dt"]]) if c["packed"] else to_dev(x.reshape(B, T, D), TDT[c["in_dt"]])
     y = gla.gla_conv1d_silu(xin, to_dev(w, torch.float32), to_dev(bias, torch.float32), conv_state=st,
                             slot_idx=torch.from_numpy(slots).to(dev()) if c["hist"] else None,

@@ -196,6 +196,7 @@ def test_page_sizes():
     assert d["layers"] * oracle.state_bytes(H, dk, dv, 2) / 1e6 < 20
 
 
+
 # --------------------------------------------------------------------------
 # backward pins
 # --------------------------------------------------------------------------

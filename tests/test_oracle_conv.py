@@ -12,9 +12,9 @@ from conftest import read_golden
 
 
 def torch_ref(x, w, bias, hist):
-    """Library reference on one sequence: pad with the history on the left,
-    depth-wise conv1d, silu.  x [L, D], w [D, 4], hist [3, D]."""
-    xt = torch.from_numpy(np.concatenate([hist, x], 0).T[None].copy())        # [1, D, L+3]
+    """Library reference on one sequence: pad with the window's last three rows
+    on the left, depth-wise conv1d, silu.  x [L, D], w [D, 4], hist [4, D]."""
+    xt = torch.from_numpy(np.concatenate([hist[1:], x], 0).T[None].copy())    # [1, D, L+3]
     a = torch.nn.functional.conv1d(xt, torch.from_numpy(w[:, None, :].copy()),
                                    torch.from_numpy(bias.copy()), groups=w.shape[0])
     return torch.nn.functional.silu(a)[0].T.numpy()                             # [L, D]
@@ -26,7 +26,7 @@ def _seqs(seed, lengths, D=6, n_slots=5):
     x = r.standard_normal((N, D))
     w = r.standard_normal((D, 4))
     bias = r.standard_normal(D)
-    state = r.standard_normal((n_slots, 3, D))
+    state = r.standard_normal((n_slots, 4, D))
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     slots = r.permutation(n_slots)[:len(lengths)].astype(np.int32)
     return x, w, bias, state, cu, slots
@@ -46,10 +46,10 @@ def pin_torch_conv(conv):
         y, st = conv(x, w, bias, cu, state, slots, init)
         for b in range(4):
             t0, t1 = cu[b], cu[b + 1]
-            hist = state[slots[b]] if init else np.zeros((3, x.shape[1]))
+            hist = state[slots[b]] if init else np.zeros((4, x.shape[1]))
             if t1 > t0:
                 np.testing.assert_allclose(y[t0:t1], torch_ref(x[t0:t1], w, bias, hist), rtol=1e-12, atol=1e-12)
-            np.testing.assert_array_equal(st[slots[b]], np.concatenate([hist, x[t0:t1]], 0)[-3:])
+            np.testing.assert_array_equal(st[slots[b]], np.concatenate([hist, x[t0:t1]], 0)[-4:])
 
 
 def pin_chaining(conv):
@@ -104,21 +104,23 @@ def _mutant(kind):
         for b in range(len(cu) - 1):
             t0, t1 = cu[b], cu[b + 1]
             use = state is not None and init_from_state and kind != "history_ignored"
-            hist = state[slots[b]] if use else np.zeros((3, D))
+            hist = state[slots[b]] if use else np.zeros((4, D))
             z = np.concatenate([hist, x[t0:t1]], 0)
+            off = 0 if kind == "oldest_row_read" else 1
             for t in range(t1 - t0):
-                a = bias + sum(w[:, j] * z[t + j] for j in range(4))
+                a = bias + sum(w[:, j] * z[t + off + j] for j in range(4))
                 y[t0 + t] = a if kind == "no_silu" else a / (1 + np.exp(-a))
             if new is not None:
-                if kind == "short_not_shifted" and t1 - t0 < 3:
-                    new[slots[b]] = np.concatenate([x[t0:t1], hist], 0)[:3]
+                if kind == "short_not_shifted" and t1 - t0 < 4:
+                    new[slots[b]] = np.concatenate([x[t0:t1], hist], 0)[:4]
                 else:
-                    new[slots[b]] = z[-3:]
+                    new[slots[b]] = z[-4:]
         return y, new
     return conv
 
 
-@pytest.mark.parametrize("kind", ["kernel_reversed", "no_silu", "history_ignored", "short_not_shifted"])
+@pytest.mark.parametrize("kind", ["kernel_reversed", "no_silu", "history_ignored", "short_not_shifted",
+                                  "oldest_row_read"])
 def test_pins_catch_planted_conv_mistakes(kind):
     failures = 0
     for pin in PINS:
