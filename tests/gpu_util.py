@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 import gen
+import oracle
 
 
 def dev():
@@ -47,3 +48,21 @@ def assert_close_bf16_out(got, ref, tol, name):
 
 def inputs(workload, seed=0, **kw):
     return gen.make_inputs(workload, seed=seed, **kw)
+
+
+def check_q16_state(m, e, m_ref, e_ref, S_ref, name):
+    """Stored state against the oracle's: equal exponents except at a
+    threshold, every value within one quantum of the coarser exponent."""
+    M = np.abs(S_ref).max(axis=-2)
+    diff = e != e_ref
+    if diff.any():
+        r = M[diff] * np.exp2(-e_ref[diff].astype(np.float64))
+        dist = np.minimum.reduce([np.abs(r / t - 1) for t in (16383.75, 16384.0, 32767.5)])
+        assert np.all(dist < 1e-6), f"{name}: exponents differ away from a threshold"
+        assert np.all(np.abs(e[diff].astype(np.int64) - e_ref[diff]) == 1)
+    quantum = np.exp2(np.maximum(e, e_ref).astype(np.float64))[..., None, :]
+    gap = np.abs(oracle.q16_decode(m, e) - oracle.q16_decode(m_ref, e_ref))
+    assert np.all(gap <= quantum), f"{name}: {np.sum(gap > quantum)} values more than a quantum apart"
+    same_e = np.broadcast_to(~diff[..., None, :], m.shape)
+    moved = np.mean(m[same_e] != m_ref[same_e])
+    print(f"  {name}: {diff.sum()} exponents differ, {moved:.2e} of mantissas differ by 1", flush=True)

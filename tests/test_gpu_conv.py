@@ -13,7 +13,7 @@ import torch
 
 import gen
 import oracle
-from gpu_util import assert_close, dev, to_dev, to_np
+from gpu_util import assert_close, check_q16_state, dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -183,4 +183,43 @@ def test_conv_window_in_the_pool_with_the_mixer_state():
         np.testing.assert_array_equal(to_np(pool.conv_view()), win_ref)
         assert_close(to_np(od), od_ref, 1e-4, "o step")
         assert_close(to_np(pool.view()), S_cur, 1e-4, "mixer states after the step")
+    pool.free()
+
+
+def test_conv_window_in_a_16bit_pool():
+    """A 16-bit pool with convolution windows: the windows (float32) and the
+    16-bit mixer states live side by side in the slots; a convolution call and
+    a decode step through the same slot indices leave each other's part
+    untouched, and both match the oracle."""
+    import linear_attention_sequence_simple_amd as gla
+    D, n_slots, n = 256, 5, 3
+    slots = np.array([4, 1, 2], np.int32)
+    x, w, bias, win0 = _inputs(11, n, D, "bf16", n_slots)
+    pool = gla.gla_state_alloc_conv(n_slots, D, fmt=gla.GLA_STATE_Q16)
+    assert pool.fmt == gla.GLA_STATE_Q16 and pool.conv_D == D
+    assert pool.seq_bytes == 16 * (96 * 192 * 2 + 192 * 4) + 4 * D * 4
+    S0 = gen.make_decode_state(n_slots, seed=12)
+    gla.gla_state_write(pool, torch.from_numpy(S0).to(dev()))
+    pool.conv_view().copy_(to_dev(win0, torch.float32))
+    m0, e0 = (t.cpu().numpy() for t in pool.q16_views())
+    sl = torch.from_numpy(slots).to(dev())
+    print("case conv window in a 16-bit pool", flush=True)
+    y = gla.gla_conv1d_silu_pool(to_dev(x[:, None], torch.bfloat16), to_dev(w, torch.float32), pool,
+                                 bias=to_dev(bias, torch.float32), slot_idx=sl, init_from_pool=True,
+                                 out_dtype=torch.float32)
+    xd = gen.make_decode_step(n, 0, seed=13)
+    o = gla.gla_recurrent_step(pool, *(to_dev(xd[c], torch.bfloat16) for c in ("q", "k", "v")),
+                               to_dev(xd["g"], torch.float32), slot_idx=sl, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref, win_ref = oracle.conv1d_silu(x, w, bias, np.arange(n + 1), win0, slots, True)
+    assert_close(to_np(y).reshape(n, D), y_ref, TOL, "y")
+    np.testing.assert_array_equal(to_np(pool.conv_view()), win_ref)
+    o_ref, m_ref, e_ref = oracle.step_q16(m0[slots], e0[slots], xd["q"], xd["k"], xd["v"], xd["g"])
+    assert_close(to_np(o), o_ref, 1e-4, "o")
+    m1, e1 = (t.cpu().numpy() for t in pool.q16_views())
+    rest = np.setdiff1d(np.arange(n_slots), slots)
+    assert np.array_equal(m1[rest], m0[rest]) and np.array_equal(e1[rest], e0[rest])
+    # the stored states of the stepped slots: within one quantum of the oracle's
+    _, S_ref = oracle.step(oracle.q16_decode(m0[slots], e0[slots]), xd["q"], xd["k"], xd["v"], xd["g"])
+    check_q16_state(m1[slots], e1[slots], m_ref, e_ref, S_ref, "state")
     pool.free()

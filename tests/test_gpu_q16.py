@@ -20,7 +20,7 @@ import torch
 
 import gen
 import oracle
-from gpu_util import assert_close, assert_close_bf16_out, dev, to_dev, to_np
+from gpu_util import assert_close, assert_close_bf16_out, check_q16_state, dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -48,24 +48,6 @@ def _read_q16(pool, slots=None):
         idx = torch.as_tensor(np.asarray(slots, np.int64), device=dev())
         m, e = m[idx], e[idx]
     return m.cpu().numpy(), e.cpu().numpy()
-
-
-def _check_state(m, e, m_ref, e_ref, S_ref, name):
-    """Stored state against the oracle's: equal exponents except at a
-    threshold, every value within one quantum of the coarser exponent."""
-    M = np.abs(S_ref).max(axis=-2)
-    diff = e != e_ref
-    if diff.any():
-        r = M[diff] * np.exp2(-e_ref[diff].astype(np.float64))
-        dist = np.minimum.reduce([np.abs(r / t - 1) for t in (16383.75, 16384.0, 32767.5)])
-        assert np.all(dist < 1e-6), f"{name}: exponents differ away from a threshold"
-        assert np.all(np.abs(e[diff].astype(np.int64) - e_ref[diff]) == 1)
-    quantum = np.exp2(np.maximum(e, e_ref).astype(np.float64))[..., None, :]
-    gap = np.abs(oracle.q16_decode(m, e) - oracle.q16_decode(m_ref, e_ref))
-    assert np.all(gap <= quantum), f"{name}: {np.sum(gap > quantum)} values more than a quantum apart"
-    same_e = np.broadcast_to(~diff[..., None, :], m.shape)
-    moved = np.mean(m[same_e] != m_ref[same_e])
-    print(f"  {name}: {diff.sum()} exponents differ, {moved:.2e} of mantissas differ by 1", flush=True)
 
 
 def test_write_read_bitwise():
@@ -133,7 +115,7 @@ def test_steps_from_stored_state(in_dtype, out_dtype):
         else:
             assert_close(to_np(o), o_ref, TOL, f"o step {step}")
         m1, e1 = _read_q16(pool)
-        _check_state(m1, e1, m_ref, e_ref, S_ref, f"state step {step}")
+        check_q16_state(m1, e1, m_ref, e_ref, S_ref, f"state step {step}")
     pool.free()
 
 
@@ -169,7 +151,7 @@ def test_slot_indices_special_decays_and_nan():
     fin = np.ones(e_ref.shape, bool)
     fin[2, 3, 11] = False
     ms, es = m1[slots], e1[slots]
-    _check_state(np.where(fin[..., None, :], ms, 0), np.where(fin, es, 0), np.where(fin[..., None, :], m_ref, 0),
+    check_q16_state(np.where(fin[..., None, :], ms, 0), np.where(fin, es, 0), np.where(fin[..., None, :], m_ref, 0),
                  np.where(fin, e_ref, 0), np.where(fin[..., None, :], S_ref, 0.0), "state")
     pool.free()
 
@@ -246,7 +228,7 @@ def test_decode_workload_sampled():
             _, S_ref = oracle.step(oracle.q16_decode(m0, e0), xs["q"], xs["k"], xs["v"], xs["g"])
             assert_close(got, o_ref, TOL, f"o step {step}")
             m1, e1 = _read_q16(pool, sample)
-            _check_state(m1, e1, m_ref, e_ref, S_ref, f"state step {step}")
+            check_q16_state(m1, e1, m_ref, e_ref, S_ref, f"state step {step}")
     print(f"  o against the float64 recurrence over {steps} steps: max|err|/rms = {worst:.3e}", flush=True)
     assert worst <= 1e-2
     pool.free()
