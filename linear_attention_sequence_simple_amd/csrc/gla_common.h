@@ -77,9 +77,12 @@ __device__ __forceinline__ bf16x8 frag_kr(const bf16* M, int pitch, int row0, in
   const bf16* p = M + (row0 + 16 * s + 4 * g + (L >> 2)) * pitch + col0 + 16 * h + 4 * (L & 3);
   return cat(lds_tr4(p), lds_tr4(p + 8 * pitch));
 }
+// (M in LDS: through an LDS-space pointer the constant part of the index
+// folds into the DS instruction's offset, so all fragments of a tile share one
+// per-lane address register.)
 __device__ __forceinline__ float frag_kr(const float* M, int pitch, int row0, int col0, int s) {
   const int l = lane_id(), g = l >> 5;
-  return M[(row0 + 8 * (s >> 2) + 4 * g + (s & 3)) * pitch + col0 + (l & 31)];
+  return ((const LDS_AS float*)M)[(row0 + 8 * (s >> 2) + 4 * g + (s & 3)) * pitch + col0 + (l & 31)];
 }
 
 // As frag_kr, in the plain contraction order (k = 16s + 8g + e).
@@ -96,7 +99,7 @@ __device__ __forceinline__ bf16x8 frag_kcP(const bf16* M, int pitch, int row0, i
 }
 __device__ __forceinline__ float frag_kcP(const float* M, int pitch, int row0, int col0, int s) {
   const int l = lane_id(), g = l >> 5;
-  return M[(row0 + (l & 31)) * pitch + col0 + 8 * (s >> 2) + 4 * g + (s & 3)];
+  return ((const LDS_AS float*)M)[(row0 + (l & 31)) * pitch + col0 + 8 * (s >> 2) + 4 * g + (s & 3)];
 }
 
 __device__ __forceinline__ bf16x8 frag_kcN(const bf16* M, int pitch, int row0, int col0, int s) {
@@ -172,8 +175,8 @@ __device__ __forceinline__ bf16x8 scale_k(bf16x8 a, const float* w, int s) {
   r[6] = (bf16)((float)a[6] * w1[2]); r[7] = (bf16)((float)a[7] * w1[3]);
   return r;
 }
-__device__ __forceinline__ float scale_k(float a, const float* w, int s) {
-  return a * w[kidx_f32(s)];
+__device__ __forceinline__ float scale_k(float a, const float* w, int s) {   // w in LDS
+  return a * ((const LDS_AS float*)w)[kidx_f32(s)];
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -91,7 +91,7 @@ struct WalkSmem {
   TIn xh[COMP ? CH * PX : 8];             // decay-weighted keys: bf16 value ...
   TIn xl[COMP ? CH * PX : 8];             // ... and bf16 residual
   TIn y[CH * PY];                         // values (reverse walk: dO), this dv-slice
-  TIn q[OUT ? CH * PQ : 8];               // queries
+  TIn q[(OUT && COMP) ? CH * PQ : 8];     // queries (the fp32 output waves read theirs from memory)
   TIn z[OUT ? DK * PZ : 8];               // state entering the chunk, [d][c]
   TIn zl[(OUT && COMP) ? DK * PZ : 8];    // residual of its bf16 copy
   // Decay tables of the current chunk and of the next one (built a chunk
@@ -270,14 +270,12 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   constexpr int DEPTH = (!OUT && COMP) ? 2 : 1;
   TileRegs<TIn, DK, NTHR> px[DEPTH];
   TileRegs<TIn, DVS, NTHR> py[DEPTH];
-  TileRegs<TIn, OUT ? DK : 8, NTHR> pq[DEPTH];
   auto prefetch = [&](auto bc, int n) {
     constexpr int B = decltype(bc)::value % DEPTH;
     const int t0 = n * CH;
     if constexpr (LOADER) {
       px[B].load(Xb, a.X.st, t0, T);
       py[B].load(Yb, a.Y.st, t0, T);
-      if constexpr (OUT) pq[B].load(Qb, a.Q.st, t0, T);
     }
   };
   constexpr std::integral_constant<int, 0> I0{};
@@ -296,9 +294,30 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       gm1 = (td < T && td >= sh) ? gb[(td - sh) * a.gst] : 0.f;
     }
   };
+  // An fp32 output wave's 32 query rows as MFMA B operands in register order
+  // (sub-step s of block kb: column 32 kb + 8 (s/4) + 4 g + s%4), read from
+  // memory a chunk ahead, four consecutive contraction values per 16-byte
+  // load; rows past T read as zero.
+  float qn[OUTW ? 3 : 1][16];
+  auto load_qn = [&](int n) {
+    if constexpr (OUTW) {
+      const int64_t t = (int64_t)n * CH + 32 * W + (lane & 31);
+      const bool live = t < T;
+      const float* p = (const float*)Qb + (live ? t : 0) * a.Q.st + 4 * g2;
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = live ? load4f(p + 32 * kb + 8 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qn[kb][4 * i + e] = v[e];
+        }
+    }
+  };
   auto step_of = [&](int i) { return n_begin + i; };
   if (nloc > 0) {
     prefetch(I0, step_of(0));
+    load_qn(step_of(0));
     if (DEPTH == 2 && nloc > 1) prefetch(I1, step_of(1));
     load_g(step_of(0));
     if (W == 0) build_decay(&sm.dec[0], gx0, gx1, gm0, gm1, OUT ? sm.utab[0] : nullptr);
@@ -316,7 +335,6 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     if constexpr (LOADER) {
       if constexpr (S::RAWX) px[B].template store<S::PX>(sm.x);
       py[B].template store<S::PY>(sm.y);
-      if constexpr (OUT) pq[B].template store<S::PQ>(sm.q);
       if constexpr (COMP)
         px[B].template store_weighted<S::PX>((bf16*)sm.xh, (bf16*)sm.xl, dc.kap);
     }
@@ -341,24 +359,39 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
     if constexpr (OUTW) {
       const int il = 32 * W + (lane & 31);          // this lane's token inside the chunk
       const float bi = dc.b2[il];
-      FT qn[3][SUB];
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-        for (int s = 0; s < SUB; ++s) qn[kb][s] = frag_kcP(sm.q, S::PQ, 32 * W, 32 * kb, s);
       // Decay-masked scores P^T (keys j in rows, queries i in columns), all
       // key blocks at once.  Off the diagonal 2^{b_i - b_j} =
       // 2^{b_i - b_{32W}} 2^{b_{32W} - b_j}, both factors <= 1.
+      // The fp32 products run in groups of 4 contraction sub-steps (48 steps
+      // over the 96-wide keys, 16 per 32-token block of P), the operands of
+      // group i+1 requested before the products of group i and the schedule
+      // fenced between groups: unfenced, the compiler requests every operand
+      // of a loop up front and spills.
+      static_assert(SUB == 16, "the walk with output here is the fp32 one");
       f32x16 acc[W + 1];
 #pragma unroll
       for (int J = 0; J <= W; ++J) acc[J] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
+      {
+        // the 4 sub-steps of a group are 4 consecutive key columns: one
+        // 16-byte read per key block
+        f32x4 xa[2][W + 1];
+        const LDS_AS float* xl = (const LDS_AS float*)sm.x + (lane & 31) * S::PX + 4 * g2;
+        auto load_x = [&](int buf, int grp) {
 #pragma unroll
           for (int J = 0; J <= W; ++J)
-            acc[J] = mfma(frag_kcP(sm.x, S::PX, 32 * J, 32 * kb, s), qn[kb][s], acc[J]);
+            xa[buf][J] = *(const LDS_AS f32x4*)(xl + 32 * J * S::PX + 32 * (grp >> 2) + 8 * (grp & 3));
+        };
+        load_x(0, 0);
+#pragma unroll
+        for (int grp = 0; grp < 12; ++grp) {
+          if (grp + 1 < 12) load_x((grp + 1) & 1, grp + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int J = 0; J <= W; ++J) acc[J] = mfma(xa[grp & 1][J][e], qn[grp >> 2][4 * (grp & 3) + e], acc[J]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       FT pf[W + 1][SUB];
       const float ri = W > 0 ? exp2f(bi - dc.b2[32 * W]) : 1.f;
 #pragma unroll
@@ -386,23 +419,50 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
       f32x16 o[NC];
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) o[cb] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
+      {
+        float za[2][NC][4];
+        auto load_z = [&](int buf, int grp) {
 #pragma unroll
           for (int cb = 0; cb < NC; ++cb)
-            o[cb] = mfma(frag_kr(sm.z, S::PZ, 32 * kb, 32 * cb, s), qn[kb][s], o[cb]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) za[buf][cb][e] = frag_kr(sm.z, S::PZ, 32 * (grp >> 2), 32 * cb, 4 * (grp & 3) + e);
+        };
+        load_z(0, 0);
+#pragma unroll
+        for (int grp = 0; grp < 12; ++grp) {
+          if (grp + 1 < 12) load_z((grp + 1) & 1, grp + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) o[cb] = mfma(za[grp & 1][cb][e], qn[grp >> 2][4 * (grp & 3) + e], o[cb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the queries are dead: request the next chunk's
+      if (it + 1 < nloc) load_qn(step_of(it + 1));
       const float lam = exp2f(dc.b2[il]);
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) o[cb] *= lam;
-#pragma unroll
-      for (int J = 0; J <= W; ++J)
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
+      {
+        constexpr int NG = 4 * (W + 1);                  // groups of 4 sub-steps over the key blocks
+        float ya[2][NC][4];
+        auto load_y = [&](int buf, int grp) {
 #pragma unroll
           for (int cb = 0; cb < NC; ++cb)
-            o[cb] = mfma(frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s), pf[J][s], o[cb]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ya[buf][cb][e] = frag_kr(sm.y, S::PY, 32 * (grp >> 2), 32 * cb, 4 * (grp & 3) + e);
+        };
+        load_y(0, 0);
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp) {
+          if (grp + 1 < NG) load_y((grp + 1) & 1, grp + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) o[cb] = mfma(ya[grp & 1][cb][e], pf[grp >> 2][4 * (grp & 3) + e], o[cb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       const int64_t trow = (int64_t)n * CH + il;
       if (a.acc.p && trow < T) {
         // add a partial sum of the same outputs (fp32, computed by another
@@ -478,23 +538,40 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
           }
         }
       } else {
+        // fp32: 4 groups of 4 sub-steps per 32-token block J, pipelined and
+        // fenced like the output products; the J loop is not unrolled, so
+        // the fragment addresses are formed once per block (unrolled, their
+        // base registers alone spill).
+        constexpr int CB_LO = T0 / 3, NCB = (T0 + NT - 1) / 3 - CB_LO + 1;
+        float bxa[2][3][4], aya[2][NCB][4];
+        auto load_s = [&](int buf, int J, int grp) {
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-#pragma unroll
-          for (int s = 0; s < SUB; ++s) {
-            FT bx[3];
+          for (int e = 0; e < 4; ++e) {
+            const int s = 4 * grp + e;
 #pragma unroll
             for (int k = 0; k < DB_N; ++k) {
               const int db = (DB_LO + k) % 3;
-              bx[db] = scale_k(frag_kr(sm.x, S::PX, 32 * J, 32 * db, s), wts + 32 * J, s);
+              bxa[buf][db][e] = scale_k(frag_kr(sm.x, S::PX, 32 * J, 32 * db, s), wts + 32 * J, s);
             }
-            FT ay = {};
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
-              if (t == 0 || db == 0) ay = frag_kr(sm.y, S::PY, 32 * J, 32 * cb, s);
-              z[t] = mfma(ay, bx[db], z[t]);
-            }
+            for (int c = 0; c < NCB; ++c) aya[buf][c][e] = frag_kr(sm.y, S::PY, 32 * J, 32 * (CB_LO + c), s);
+          }
+        };
+        load_s(0, 0, 0);
+#pragma unroll 1
+        for (int J = 0; J < 4; ++J) {
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            if (grp + 1 < 4) load_s((grp + 1) & 1, J, grp + 1);
+            else if (J + 1 < 4) load_s(0, J + 1, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int t = 0; t < NT; ++t) {
+                const int cb = (T0 + t) / 3, db = (T0 + t) % 3;
+                z[t] = mfma(aya[grp & 1][cb - CB_LO][e], bxa[grp & 1][db][e], z[t]);
+              }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
