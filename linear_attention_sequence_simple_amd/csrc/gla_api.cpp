@@ -194,14 +194,6 @@ FwdPlan plan_fwd(const gla_dims* d) {
   p.n_chunks = (int)((d->T + CH - 1) / CH);
   const int64_t walkers = d->B * d->H * p.ns;
   p.nseg = plan_segments(walkers, p.n_chunks, d->segments);
-  // fp32 walks: a chunk of the output walk costs about three of the
-  // state-only walk (31 against 10 us at B=1, T=2048), so once the launch is
-  // segmented anyway one chunk per segment shortens the chain most, as long
-  // as the output pass stays within four rounds of the chip (measured 161
-  // against 177 us for the default plan)
-  if (!in_bf16 && p.nseg > 1 && d->segments <= 0 &&
-      walkers * p.n_chunks <= 4 * kTargetWorkgroups)
-    p.nseg = p.n_chunks;
   p.cps = (p.n_chunks + p.nseg - 1) / p.nseg;
   p.nseg = (p.n_chunks + p.cps - 1) / p.cps;
   const int64_t BH = d->B * d->H;
