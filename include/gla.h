@@ -378,8 +378,8 @@ gla_status gla_recurrent_step(int64_t B, int32_t H, int32_t dk, int32_t dv,
  *   dq, dk : [B, T, H, dk] out_dtype      dv : [B, T, H, dv] out_dtype
  *   dg   : [B, T, H] float32              dS0 : [B, H, dk, dv] float32 or NULL (not written)
  *   ws   : at least gla_workspace_size(GLA_OP_BWD) bytes.
- * The library implements in_dtype = GLA_BF16 and T <= 131,072 (1,024 chunks;
- * UNSUPPORTED otherwise).
+ * in_dtype is GLA_BF16 or GLA_F32 (q, k, v and dO alike); T <= 131,072
+ * (1,024 chunks; UNSUPPORTED otherwise).
  */
 gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k,
                          const void* v, const float* g, const float* S0,

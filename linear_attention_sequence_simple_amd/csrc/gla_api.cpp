@@ -355,16 +355,26 @@ BwdPlan plan_bwd(const gla_dims* d) {
 // fp32 backward workspace: the first dv-half's sums of dq and dk
 // ([B,T,H,DK] each), the float32 gradients when the outputs are bf16, q.dq
 // and k.dk ([B,T,H] each), the final forward state, the per-chunk sums of the
-// log-decay gradient.  Its walks run whole sequences (no segment plan).
+// log-decay gradient, and the segment states and decays of both recurrences
+// when the walks are split.  Every walk has three slices (32 value columns
+// for dq and dk, 64 for dv), so one segment plan serves them all.
 struct BwdF32Plan {
   int n_chunks;
-  size_t off_adq, off_adk, off_fdq, off_fdk, off_rq, off_rk, off_st, off_r, ws_total;
+  SegPlan sp;
+  size_t off_adq, off_adk, off_fdq, off_fdk, off_rq, off_rk, off_st, off_r, off_segf, off_segr, off_decf, off_decr,
+      ws_total;
 };
 
 BwdF32Plan plan_bwd_f32(const gla_dims* d) {
   BwdF32Plan p{};
   p.n_chunks = (int)((d->T + CH - 1) / CH);
   const int64_t BH = d->B * d->H;
+  p.sp.n_chunks = p.n_chunks;
+  p.sp.ns = 3;
+  p.sp.nseg = plan_segments(BH * p.sp.ns, p.n_chunks, d->segments);
+  p.sp.cps = (p.n_chunks + p.sp.nseg - 1) / p.sp.nseg;
+  p.sp.nseg = (p.n_chunks + p.sp.cps - 1) / p.sp.cps;
+  p.sp.fine = fine_factor(2 * BH * p.sp.ns * (p.sp.nseg - 1), p.sp.cps, false);
   const size_t part = align256((size_t)d->B * d->T * d->H * DK * sizeof(float));
   const size_t tok = align256((size_t)d->B * d->T * d->H * sizeof(float));
   const bool bf16_out = d->out_dtype == GLA_BF16;
@@ -377,15 +387,14 @@ BwdF32Plan plan_bwd_f32(const gla_dims* d) {
   p.off_rk = off; off += tok;
   p.off_st = off; off += align256((size_t)BH * kStateElems * sizeof(float));
   p.off_r = off; off += align256((size_t)BH * (p.n_chunks + 1) * sizeof(float));
+  const size_t seg = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * kStateElems * sizeof(float)) : 0;
+  const size_t dec = p.sp.nseg > 1 ? align256((size_t)BH * p.sp.entries() * sizeof(float)) : 0;
+  p.off_segf = off; off += seg;
+  p.off_segr = off; off += seg;
+  p.off_decf = off; off += dec;
+  p.off_decr = off; off += dec;
   p.ws_total = off;
   return p;
-}
-
-gla_status check_bwd_f32_plan(const gla_dims* d) {
-  if (d->segments > 1)
-    return fail(GLA_ERR_UNSUPPORTED, "the fp32 backward walks whole sequences: segments must be 0 or 1 (got %d)",
-                d->segments);
-  return GLA_OK;
 }
 
 // A view with caller strides (elements), in dv-slices of `slice_w` columns.
@@ -594,8 +603,8 @@ gla_status scratch_ptr(void** out) {
 gla_status bwd_f32(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g, const float* S0,
                    const void* dO, const float* dS_T, void* dq, void* dk, void* dv, float* dg, float* dS0, void* ws,
                    size_t ws_bytes, void* stream) {
-  TRY(check_bwd_f32_plan(dims));
   const BwdF32Plan p = plan_bwd_f32(dims);
+  const SegPlan& sp = p.sp;
   if (ws_bytes < p.ws_total) return fail(GLA_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, p.ws_total);
   TRY(check_ptr(ws, "ws", false));
   if (p.n_chunks > 1024) return fail(GLA_ERR_UNSUPPORTED, "the backward supports at most 1024 chunks (T <= 131072)");
@@ -613,9 +622,7 @@ gla_status bwd_f32(const gla_dims* dims, const void* q, const void* k, const voi
   float* rq = (float*)(w + p.off_rq);
   float* rk = (float*)(w + p.off_rk);
   float* S_T = (float*)(w + p.off_st);
-  constexpr int hw = 96, sw = 32;                 // dv-half and value-slice widths
-  const int nq = DK / sw;                         // value slices of dq and dk walks
-  const SegPlan whole{nq, 1, p.n_chunks, p.n_chunks, 1};
+  constexpr int hw = 96, sw = 32, dw = 64;       // dv-half, dq/dk value-slice and dv value-slice widths
   // states of the dq and dk walks: element (x = column of a dv-half, y =
   // row of S) of value slice s, i.e. S[32 s + y][half + x]
   auto tview = [&](const float* base) { return StateView{const_cast<float*>(base), kStateElems, 0, (int64_t)sw * DV, 1, DV}; };
@@ -630,6 +637,36 @@ gla_status bwd_f32(const gla_dims* dims, const void* q, const void* k, const voi
     a.H = dims->H;
   };
   hipError_t e = hipSuccess;
+  // With segments: the state entering every segment, of the forward
+  // recurrence S (keys k, values v) and of the backward-in-time one U (keys
+  // q, values dO, log-decay shifted), from state-only walks over 64-column
+  // value slices and a scan, in the plain [dk][dv] layout of S0 and dS_T; the
+  // walks below read them through their own views.
+  float* seg_f = sp.nseg > 1 ? (float*)(w + p.off_segf) : nullptr;
+  float* seg_r = sp.nseg > 1 ? (float*)(w + p.off_segr) : nullptr;
+  if (sp.nseg > 1) {
+    WalkArgs fs{};
+    fs.X = tok_view(k, 4, dims, DK, 0, false);
+    fs.Y = tok_view(v, 4, dims, DV, dw, false);
+    common(fs, false);
+    WalkArgs rs{};
+    rs.X = tok_view(q, 4, dims, DK, 0, true);
+    rs.Y = tok_view(dO, 4, dims, DV, dw, true);
+    common(rs, true);
+    e = segment_states(fs, WV_FWD_STATE_F32, sp, S0, nullptr, dims->H, seg_view(seg_f, state_plain(nullptr, dw), sp.entries()),
+                       (float*)(w + p.off_decf), BH, st);
+    if (e == hipSuccess)
+      e = segment_states(rs, WV_FWD_STATE_F32, sp, dS_T, nullptr, dims->H,
+                         seg_view(seg_r, state_plain(nullptr, dw), sp.entries()), (float*)(w + p.off_decr), BH, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd segment states");
+  }
+  // a walk's entering states: the segment states through the walk's view, or
+  // the initial state itself (or none) with one segment
+  auto entering = [&](StateView lay, float* seg, const float* z0) {
+    if (sp.nseg > 1) return coarse(seg_view(seg, lay, sp.entries()), sp);
+    lay.p = const_cast<float*>(z0);
+    return z0 ? lay : StateView{};
+  };
   for (int hh = 0; hh < 2 && e == hipSuccess; ++hh) {
     // dq: forward recurrence with keys a dv-half of v, values k, queries the
     // same half of dO; its state is S^T restricted to the half
@@ -640,9 +677,9 @@ gla_status bwd_f32(const gla_dims* dims, const void* q, const void* k, const voi
     f.O = tok_view(hh == 0 ? adq : fdq, 4, dims, DK, sw, false);
     if (hh == 1) f.acc = tok_view(adq, 4, dims, DK, sw, false);
     common(f, false);
-    const StateView fz0 = shifted(tview(S0), (int64_t)hh * hw);
     const StateView fzT = shifted(tview(dS_T ? S_T : nullptr), (int64_t)hh * hw);
-    e = walk_segments(f, WV_OUT_F32_NC1, whole, S0 ? fz0 : StateView{}, dS_T ? fzT : StateView{}, BH, st);
+    e = walk_segments(f, WV_OUT_F32_NC1, sp, shifted(entering(tview(nullptr), seg_f, S0), (int64_t)hh * hw),
+                      dS_T ? fzT : StateView{}, BH, st);
     if (e != hipSuccess) break;
     // dk: backward in time, keys the half of dO, values q, queries the same
     // half of v; its state is the state gradient's transpose
@@ -653,23 +690,21 @@ gla_status bwd_f32(const gla_dims* dims, const void* q, const void* k, const voi
     r.O = tok_view(hh == 0 ? adk : fdk, 4, dims, DK, sw, true);
     if (hh == 1) r.acc = tok_view(adk, 4, dims, DK, sw, true);
     common(r, true);
-    const StateView rz0 = shifted(tview(dS_T), (int64_t)hh * hw);
-    e = walk_segments(r, WV_OUT_F32_NC1, whole, dS_T ? rz0 : StateView{}, StateView{}, BH, st);
+    e = walk_segments(r, WV_OUT_F32_NC1, sp, shifted(entering(tview(nullptr), seg_r, dS_T), (int64_t)hh * hw),
+                      StateView{}, BH, st);
   }
   if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq/dk walks");
   // dv: backward in time, keys q, values dO (64-column slices), queries k;
   // the final state is the gradient leaving the first token
   {
-    const int dw = 64;
     WalkArgs a{};
     a.X = tok_view(q, 4, dims, DK, 0, true);
     a.Y = tok_view(dO, 4, dims, DV, dw, true);
     a.Q = tok_view(k, 4, dims, DK, 0, true);
     a.O = tok_view(dv, bf16_out ? 2 : 4, dims, DV, dw, true);
     common(a, true);
-    const SegPlan whole_v{DV / dw, 1, p.n_chunks, p.n_chunks, 1};
-    e = walk_segments(a, bf16_out ? WV_FWD_OUT_F32_BF16 : WV_FWD_OUT_F32_F32, whole_v, state_plain(const_cast<float*>(dS_T), dw),
-                      state_plain(dS0, dw), BH, st);
+    e = walk_segments(a, bf16_out ? WV_FWD_OUT_F32_BF16 : WV_FWD_OUT_F32_F32, sp,
+                      entering(state_plain(nullptr, dw), seg_r, dS_T), state_plain(dS0, dw), BH, st);
     if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dv walk");
   }
   RowDotsArgs rd{(const float*)q, (const float*)k, fdq, fdk, rq, rk, bf16_out ? (__bf16*)dq : nullptr,
@@ -790,12 +825,7 @@ gla_status gla_workspace_size(int32_t op, const gla_dims* dims, size_t* bytes) {
     return ok();
   }
   if (op == GLA_OP_BWD) {
-    if (dims->in_dtype == GLA_F32) {
-      TRY(check_bwd_f32_plan(dims));
-      *bytes = plan_bwd_f32(dims).ws_total;
-    } else {
-      *bytes = plan_bwd(dims).ws_total;
-    }
+    *bytes = dims->in_dtype == GLA_F32 ? plan_bwd_f32(dims).ws_total : plan_bwd(dims).ws_total;
     return ok();
   }
   if (op == GLA_OP_FWD_VARLEN_Q16) {

@@ -59,11 +59,12 @@ def test_workspace_sizes(L):
     tokens = 2 * 300 * 16
     assert n >= 2 * tokens * 96 * 4 + 2 * tokens * 4
     # fp32 inputs: first-half sums, float32 gradients for bf16 outputs, dot
-    # products, the final state and chunk sums; whole sequences only
-    st, n32 = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32, out_dtype=gla.GLA_BF16))
+    # products, the final state and chunk sums, and with segments the states
+    # and decays entering them, of both recurrences
+    st, n32 = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32, out_dtype=gla.GLA_BF16, segments=1))
     assert st == 0 and n32 >= 4 * tokens * 96 * 4 + 2 * tokens * 4
-    st, _ = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32, segments=2))
-    assert st == 2 and "whole sequences" in L.gla_last_error().decode()
+    st, n32s = ws_size(L, gla.GLA_OP_BWD, dims(in_dtype=gla.GLA_F32, out_dtype=gla.GLA_BF16, segments=3))
+    assert st == 0 and n32s - n32 >= 2 * 2 * 16 * 3 * 96 * 192 * 4
     st, _ = ws_size(L, 7, dims())
     assert st == 1
     # a packed prefill into a 16-bit pool stages one float32 state per

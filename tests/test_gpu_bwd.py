@@ -118,14 +118,14 @@ def test_longest_supported_sequence():
 TOL_F32 = 1e-4
 
 
-def run_bwd_f32(d, S0=True, dS_T=True, out_dtype=torch.float32):
+def run_bwd_f32(d, S0=True, dS_T=True, out_dtype=torch.float32, segments=None):
     import linear_attention_sequence_simple_amd as gla
     r = gla.gla_chunk_bwd(to_dev(d["q"], torch.float32), to_dev(d["k"], torch.float32),
                           to_dev(d["v"], torch.float32), to_dev(d["g"], torch.float32),
                           to_dev(d["dO"], torch.float32),
                           S0=to_dev(d["S0"], torch.float32) if S0 else None,
                           dS_T=to_dev(d.get("dS_T"), torch.float32) if dS_T else None,
-                          out_dtype=out_dtype, want_dS0=True)
+                          out_dtype=out_dtype, want_dS0=True, segments=segments)
     torch.cuda.synchronize()
     return [to_np(x) for x in r]
 
@@ -160,6 +160,17 @@ def test_f32_special_decays(g):
     check_f32(d, run_bwd_f32(d))
 
 
+@pytest.mark.parametrize("T,segments,s0,dst", [(1024, 4, True, True), (1000, 3, False, True), (640, 5, True, False),
+                                               (300, 1, True, True)])
+def test_f32_segments(T, segments, s0, dst):
+    """The fp32 backward's segment plan: state-only walks of both recurrences
+    and a scan give every segment's entering state; one segment is the whole
+    sequence."""
+    d = inputs("fwd_f32_b1_t2048", seed=80 + segments, B=1, T=T, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
+    print(f"case bwd fp32 T={T} segments={segments} S0={s0} dS_T={dst}", flush=True)
+    check_f32(d, run_bwd_f32(d, s0, dst, segments=segments), s0, dst)
+
+
 def test_f32_training_shape():
     """B=1, H=16, T=2048 (the fp32 workload's shape), every gradient of every
     head against the oracle."""
@@ -177,3 +188,19 @@ def test_f32_bf16_gradients():
         assert_close_bf16_out(x, y, TOL_F32, name + "(bf16)")
     assert_close(got[3], ref[3], TOL_F32, "dg")
     assert_close(got[4], ref[4], TOL_F32, "dS0")
+
+
+@pytest.mark.parametrize("eq,ek,ev,edo", [(15, -15, 10, -10), (-10, -10, 20, 20)])
+def test_input_magnitudes(eq, ek, ev, edo):
+    """bf16 q, k, v and dO scaled by powers of two far from unit scale: the
+    gradients keep the unit-scale error relative to their rms."""
+    d = inputs("bwd_bf16_b4_t4096", seed=12, B=1, T=300, H=2, with_dO=True, with_dS_T=True,
+               S0="normal0.1")
+    d["q"] = d["q"] * 2.0 ** eq
+    d["k"] = d["k"] * 2.0 ** ek
+    d["v"] = d["v"] * 2.0 ** ev
+    d["dO"] = d["dO"] * 2.0 ** edo
+    d["S0"] = d["S0"] * 2.0 ** (ek + ev)
+    d["dS_T"] = d["dS_T"] * 2.0 ** (eq + edo)
+    print(f"case bwd magnitudes 2^{eq}, 2^{ek}, 2^{ev}, 2^{edo}", flush=True)
+    check(d, run_bwd(d))

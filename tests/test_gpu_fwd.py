@@ -170,3 +170,25 @@ def test_deterministic_and_chaining():
     ob, Sb = run_fwd(b, torch.bfloat16, torch.float32)
     assert_close(np.concatenate([oa, ob], 1), o1, 1e-4, "chained o")
     assert_close(Sb, S1, 1e-4, "chained S")
+
+
+@pytest.mark.parametrize("eq,ek,ev", [(20, 20, 20), (-20, -20, -20), (30, -30, 12), (-12, 0, 40)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_input_magnitudes(eq, ek, ev, dtype):
+    """q, k and v scaled by powers of two across fp32's exponent range (exact
+    in bf16 too): bf16 keeps fp32's exponent range, so the compensated bf16
+    pairs of P, the state copy and the weighted keys hold their 16 significant
+    bits at any scale, and the error relative to the output's rms stays where
+    it is at unit scale."""
+    d = inputs("fwd_bf16_b8_t2048", seed=11, B=1, T=300, H=2, S0="normal0.1")
+    d["q"] = d["q"] * 2.0 ** eq
+    d["k"] = d["k"] * 2.0 ** ek
+    d["v"] = d["v"] * 2.0 ** ev
+    d["S0"] = d["S0"] * 2.0 ** (ek + ev)
+    print(f"case magnitudes 2^{eq}, 2^{ek}, 2^{ev} {dtype}", flush=True)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o, S = run_fwd(d, dt, torch.float32)
+    o_ref, S_ref = oracle.forward(d["q"], d["k"], d["v"], d["g"], d["S0"])
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert_close(o, o_ref, tol, "o")
+    assert_close(S, S_ref, tol, "S_T")
