@@ -636,7 +636,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 // overlaps the products.  All tiles are read from memory with row-contiguous
 // 16-byte accesses, spread over both phases so that the workgroups on the
 // chip keep the memory busy instead of all loading at the same moment.
-template <class TOut, int W, bool PACKED, bool GATED>
+template <class TOut, int W, bool PACKED, bool GATED, bool ACC>
 __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3, true>& sm, int b, int h,
                                              int slice, int seg) {
   using S = WalkSmem<bf16, 3, true>;
@@ -875,11 +875,25 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
       bf16x8 yv[2][NC];
       bf16x4 gt[GATED ? NC : 1][4];
       const int64_t grow = (int64_t)n * CH + 32 * W + (lane & 31);
+      // ACC walks add a partial sum of the same outputs (fp32, computed by
+      // another walk over the other half of a contraction): this lane's row
+      // is requested before the last key block's products (any earlier, its
+      // 48 registers spill)
+      f32x4 av[ACC ? NC : 1][4];
 #pragma unroll
       for (int cb = 0; cb < NC; ++cb) yv[0][cb] = sfrag_kr(sm.y, 0, 32 * cb, 0);
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
         const int bf = k & 1, J = k >> 1, s = k & 1;
+        if (ACC && k == NK - 1) {
+          const bool live = grow < T;
+          const float* ap = (const float*)a.acc.p + b * a.acc.sb + sq.t0 * a.acc.st + h * a.acc.sh +
+                            (live ? grow : 0) * a.acc.st + 4 * g2;
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) av[cb][qq] = live ? load4f(ap + 32 * cb + 8 * qq) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if (GATED && k == NK - 2) {
           const bool live = grow < T;
           const bf16* gp = (const bf16*)a.G.p + b * a.G.sb + sq.t0 * a.G.st + h * a.G.sh +
@@ -899,21 +913,17 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
           o[cb] = mfma(yv[bf][cb], pl[J][s], o[cb]);
         }
       }
-      if (a.acc.p) {
-        // Add a partial sum of the same outputs (fp32, computed by another
-        // walk over the other half of a contraction) and, when asked, write
-        // the dot product of each output row with a row of D.
-        const int64_t trow = (int64_t)n * CH + 32 * W + (lane & 31);
+      if constexpr (ACC) {
+        // add the partial sum and, when asked, write the dot product of each
+        // output row with a row of D
+        const int64_t trow = grow;
         const bool live = trow < T;
-        const float* ap = (const float*)a.acc.p + b * a.acc.sb + sq.t0 * a.acc.st + h * a.acc.sh + trow * a.acc.st + 4 * g2;
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const f32x4 v = live ? load4f(ap + 32 * cb + 8 * qq) : f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] += v[e];
-          }
+            for (int e = 0; e < 4; ++e) o[cb][4 * qq + e] += av[cb][qq][e];
         if (a.rdot.p) {
           const bf16* dp = (const bf16*)a.D.p + b * a.D.sb + sq.t0 * a.D.st + h * a.D.sh + trow * a.D.st + 4 * g2;
           float r = 0.f;
@@ -1057,7 +1067,7 @@ __device__ __forceinline__ int longest_first(const WalkArgs& a, int i) {
 }
 
 // The walk of workgroup `local` of a launch of `nwg` workgroups.
-template <class TIn, class TOut, int NC, int MODE, bool PACKED = false, bool GATED = false>
+template <class TIn, class TOut, int NC, int MODE, bool PACKED = false, bool GATED = false, bool ACC = false>
 __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, MODE == WALK_FWD_OUT>& sm, int local,
                                            int nwg) {
   // Work item order: slice fastest, then segment, head, batch.  Equal-length
@@ -1084,14 +1094,14 @@ __device__ __forceinline__ void walk_block(const WalkArgs& a, WalkSmem<TIn, NC, 
   if constexpr (PACKED) b = longest_first(a, b);
   if constexpr (MODE == WALK_FWD_OUT && std::is_same<TIn, bf16>::value) {
     switch (threadIdx.x >> 6) {
-      case 0: prefill_wave<TOut, 0, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      case 1: prefill_wave<TOut, 1, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      case 2: prefill_wave<TOut, 2, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      case 3: prefill_wave<TOut, 3, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      case 4: prefill_wave<TOut, 4, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      case 5: prefill_wave<TOut, 5, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      case 6: prefill_wave<TOut, 6, PACKED, GATED>(a, sm, b, h, slice, seg); break;
-      default: prefill_wave<TOut, 7, PACKED, GATED>(a, sm, b, h, slice, seg); break;
+      case 0: prefill_wave<TOut, 0, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      case 1: prefill_wave<TOut, 1, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      case 2: prefill_wave<TOut, 2, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      case 3: prefill_wave<TOut, 3, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      case 4: prefill_wave<TOut, 4, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      case 5: prefill_wave<TOut, 5, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      case 6: prefill_wave<TOut, 6, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
+      default: prefill_wave<TOut, 7, PACKED, GATED, ACC>(a, sm, b, h, slice, seg); break;
     }
     return;
   } else {
@@ -1200,6 +1210,8 @@ static hipError_t launch_one(const WalkArgs& a, int nwg, hipStream_t st) {
 }
 
 hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st) {
+  // the bf16 walks add partial sums only in the pair launch built for it
+  if (a.acc.p && (variant == WV_FWD_OUT_BF16_BF16 || variant == WV_FWD_OUT_BF16_F32)) return hipErrorInvalidValue;
   switch (variant) {
     case WV_FWD_OUT_BF16_BF16: return launch_one<bf16, bf16, 3, WALK_FWD_OUT>(a, nwg, st);
     case WV_FWD_OUT_BF16_F32: return launch_one<bf16, float, 3, WALK_FWD_OUT>(a, nwg, st);
@@ -1212,21 +1224,29 @@ hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st) 
   }
 }
 
-template <class TOut>
+template <class TOut, bool ACC>
 __global__ void __launch_bounds__(WalkShape<WALK_FWD_OUT>::THREADS, 1)
     walk_out_pair_kernel(WalkArgs a0, WalkArgs a1, int nwg0) {
   __shared__ WalkSmem<bf16, 3, true> sm;
   if ((int)blockIdx.x < nwg0)
-    walk_block<bf16, TOut, 3, WALK_FWD_OUT>(a0, sm, (int)blockIdx.x, nwg0);
+    walk_block<bf16, TOut, 3, WALK_FWD_OUT, false, false, ACC>(a0, sm, (int)blockIdx.x, nwg0);
   else
-    walk_block<bf16, TOut, 3, WALK_FWD_OUT>(a1, sm, (int)blockIdx.x - nwg0, (int)gridDim.x - nwg0);
+    walk_block<bf16, TOut, 3, WALK_FWD_OUT, false, false, ACC>(a1, sm, (int)blockIdx.x - nwg0, (int)gridDim.x - nwg0);
 }
 
 hipError_t launch_out_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, int out_bf16,
                                 hipStream_t st) {
   const dim3 grid(nwg0 + nwg1), block(WalkShape<WALK_FWD_OUT>::THREADS);
-  if (out_bf16) hipLaunchKernelGGL((walk_out_pair_kernel<bf16>), grid, block, 0, st, a0, a1, nwg0);
-  else hipLaunchKernelGGL((walk_out_pair_kernel<float>), grid, block, 0, st, a0, a1, nwg0);
+  // both walks add partial sums (a compile-time variant), or neither
+  if ((a0.acc.p != nullptr) != (a1.acc.p != nullptr)) return hipErrorInvalidValue;
+  const bool acc = a0.acc.p != nullptr;
+  if (out_bf16) {
+    if (acc) hipLaunchKernelGGL((walk_out_pair_kernel<bf16, true>), grid, block, 0, st, a0, a1, nwg0);
+    else hipLaunchKernelGGL((walk_out_pair_kernel<bf16, false>), grid, block, 0, st, a0, a1, nwg0);
+  } else {
+    if (acc) hipLaunchKernelGGL((walk_out_pair_kernel<float, true>), grid, block, 0, st, a0, a1, nwg0);
+    else hipLaunchKernelGGL((walk_out_pair_kernel<float, false>), grid, block, 0, st, a0, a1, nwg0);
+  }
   return hipGetLastError();
 }
 
