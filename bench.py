@@ -9,7 +9,8 @@ bf16 output.  One step = one gla_chunk_fwd call over that batch, inputs
 resident in HBM.  The same line carries, measured in the same run:
   decode    batched decode step, 1,280 sequences x 24 layers x 64 steps,
             fp32 state read and written in place (GB/s of state traffic)
-  backward  chunked backward, B=4, H=16, T=4096 (tokens/s)
+  backward  chunked backward, B=4, H=16, T=4096 (tokens/s), and on fp32
+            inputs and outputs at B=1, T=2048 (backward.fp32)
   long_context  prefill B=1, T=65536 with a non-zero initial state
   packed    serving prefill: 16 prompts of 2,048-8,192 tokens packed along
             one token axis, final states written into a 1,280-slot pool
@@ -799,7 +800,27 @@ def bench_backward(torch, gla, steps, warmup):
             "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
             "mfma_ceiling": mfma_ceiling(flops, nbytes, BF16_PEAK_TFLOPS),
             "kernels_per_call": "8: paired pass-1 state walks, 2 segment scans, dq/dv/dk walks, "
-                                "partial-sum finish, d-log-decay finish"}
+                                "partial-sum finish, d-log-decay finish",
+            "fp32": bench_backward_f32(torch, gla, steps, warmup)}
+
+
+def bench_backward_f32(torch, gla, steps, warmup):
+    """The backward on fp32 inputs and outputs at the fp32 workload's shape
+    (B=1, T=2048, H=16), on the fp32 matrix cores."""
+    d = gen.make_inputs("fwd_f32_b1_t2048", seed=0, with_dO=True)
+    B, T = d["meta"]["B"], d["meta"]["T"]
+    q, k, v, g, S0, dO = _dev_inputs(torch, d, torch.float32)
+    dims = gla.GlaDims(B, T, H, DK, DV, CH, gla.GLA_F32, gla.GLA_F32)
+    ws = torch.empty(gla.gla_workspace_size(gla.GLA_OP_BWD, dims), dtype=torch.uint8, device=q.device)
+    fn = lambda: gla.gla_chunk_bwd(q, k, v, g, dO, out_dtype=torch.float32, workspace=ws)
+    ms, _ = _time_calls(torch, fn, steps, warmup, warm_ms=30)
+    nbytes = bwd_bytes(B, T, 4, 4)
+    flops = BWD_FLOP_PER_TH * B * T * H
+    return {"workload": f"backward B={B} T={T} H=16 fp32 in/out, fp32 dg, S0 = dS_T = 0",
+            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "GBps_algorithmic": nbytes / (ms * 1e-3) / 1e9,
+            "mfma_util": flops / (ms * 1e-3) / (F32_MFMA_PEAK_TFLOPS * 1e12), "mfma_peak": f"fp32 {F32_MFMA_PEAK_TFLOPS} TFLOP/s",
+            "kernels_per_call": "state-only walks of both recurrences, 2 segment scans, 4 dq/dk walks, the dv walk, "
+                                "row dots, partial-sum finish, d-log-decay finish"}
 
 
 def src_digest():
