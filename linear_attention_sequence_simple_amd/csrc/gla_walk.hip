@@ -617,8 +617,9 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 }
 
 // bf16 prefill with output: 8 waves.  For chunk n (decay tables dec[n&1]):
-//   phase 1  output waves: stage their own 32 query rows, decay-masked scores
-//                          P from the queries and keys, and
+//   phase 1  output waves: decay-masked scores P from their 32 queries (in
+//                          registers, read from memory a chunk ahead) and
+//                          the keys, and
 //                          O = diag(Lambda) (Q S_n) from the published bf16
 //                          value/residual copy of S_n; wave 0 then builds
 //                          the decay tables of chunk n+1 in the other buffer
@@ -635,7 +636,8 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
 // there for the next chunk, have two) and the staging
 // overlaps the products.  All tiles are read from memory with row-contiguous
 // 16-byte accesses, spread over both phases so that the workgroups on the
-// chip keep the memory busy instead of all loading at the same moment.
+// chip keep the memory busy instead of all loading at the same moment.  The
+// query rows of the LDS tile serve only the bf16 output's transpose.
 template <class TOut, int W, bool PACKED, bool GATED, bool ACC>
 __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3, true>& sm, int b, int h,
                                              int slice, int seg) {
@@ -688,25 +690,21 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
 
   TileRegs<bf16, DK, NTHR> px;                          // keys of the chunk being staged
   TileRegs<bf16, DVS, NTHR> py;                         // and its values
-  // an output wave's 32 query rows: lane l loads half of row l/2, 96
-  // contiguous bytes as 6 pieces of 16 at immediate offsets from one 32-bit
-  // lane offset, under one row check (per-piece offsets would be held as
-  // 64-bit values across the chunk loop and spilled)
-  uint4 qr[OUTW ? 6 : 1];
-  const int qrow = lane >> 1, qcol = 48 * (lane & 1);
+  // an output wave's 32 query rows, read from memory a chunk ahead straight
+  // into the plain-order MFMA B operands (lane l: row l%32, columns
+  // 32 kb + 16 s + 8 (l/32) .. +7): 6 pieces of 16 bytes at immediate offsets
+  // from one 32-bit lane offset, under one row check (per-piece offsets would
+  // be held as 64-bit values across the chunk loop and spilled)
+  bf16x8 qcur[OUTW ? 3 : 1][2];
   auto load_q = [&](int n) {
     if constexpr (OUTW) {
       const int64_t t0 = (int64_t)n * CH + 32 * W;
-      const char* p = tile_base(Qb, a.Q.st, t0, 32) + row_offset<bf16>(qrow, qcol, a.Q.st, 32);
-      const bool live = t0 + qrow < T;
+      const char* p = tile_base(Qb, a.Q.st, t0, 32) + row_offset<bf16>(lane & 31, 8 * g2, a.Q.st, 32);
+      const bool live = t0 + (lane & 31) < T;
 #pragma unroll
-      for (int i = 0; i < 6; ++i) qr[i] = live ? *(const uint4*)(p + 16 * i) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stage_q = [&]() {
-    if constexpr (OUTW) {
+      for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
-      for (int i = 0; i < 6; ++i) *(uint4*)(sm.q + swz96(32 * W + qrow, qcol + 8 * i)) = qr[i];
+        for (int s = 0; s < 2; ++s) qcur[kb][s] = live ? *(const bf16x8*)(p + 2 * (32 * kb + 16 * s)) : bf16x8{};
     }
   };
   // publish the state as a bf16 value/residual pair
@@ -766,14 +764,6 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
     if constexpr (OUTW) {
       const int il = 32 * W + (lane & 31);            // this lane's token inside the chunk
       const float bi = dc.b2[il];
-      // this wave's 32 queries as plain-order MFMA B operands (the wave reads
-      // back only the rows it wrote itself)
-      stage_q();
-      bf16x8 qcur[3][2];
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) qcur[kb][s] = sfrag_kcN(sm.q, 32 * W, 32 * kb, s);
       // O^T = diag(Lambda) (Z^T Q^T), operands of step k+1 requested before
       // the products of step k
 #pragma unroll
