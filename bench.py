@@ -799,7 +799,7 @@ def bench_backward(torch, gla, steps, warmup):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "mfma_util": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
             "mfma_ceiling": mfma_ceiling(flops, nbytes, BF16_PEAK_TFLOPS),
-            "kernels_per_call": "8: paired pass-1 state walks, 2 segment scans, dq/dv/dk walks, "
+            "kernels_per_call": "5: three launches of the dq, dk and dv walks over two staggered segments, "
                                 "partial-sum finish, d-log-decay finish",
             "fp32": bench_backward_f32(torch, gla, steps, warmup)}
 

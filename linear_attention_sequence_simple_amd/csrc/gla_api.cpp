@@ -1089,6 +1089,32 @@ gla_status gla_conv1d_silu_pool(int64_t B, int64_t T, int32_t in_dtype, int32_t 
                    pool->n_slots, slot_idx, init_from_pool, y, stream, "gla_conv1d_silu_pool");
 }
 
+}  // extern "C"
+
+namespace {
+// The log-decay gradient of the bf16 backward from the dot products q.dq and
+// k.dk the second-half walks left per token: in-chunk suffix sums, then the
+// later chunks' totals and <dS_T, S_T>; dS0 through the first decay.
+gla_status bwd_tail(const gla_dims* dims, const BwdPlan& p, const float* rq, const float* rk, float* dg,
+                    const float* dS_T, const float* S_T, float* dS0, const float* g, char* w, hipStream_t st) {
+  BwdFinishArgs fa{};
+  fa.rq = rq;
+  fa.rk = rk;
+  fa.dg = dg;
+  fa.chunk_r = (float*)(w + p.off_r);
+  fa.B = dims->B;
+  fa.T = dims->T;
+  fa.H = dims->H;
+  fa.n_chunks = p.sp.n_chunks;
+  hipError_t e = launch_bwd_finish(fa, st);
+  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd finish");
+  e = launch_dg_finish(dg, fa.chunk_r, dS_T, S_T, dS0, g, dims->B, dims->T, dims->H, p.sp.n_chunks, st);
+  return device_err(e, "gla_chunk_bwd dg finish");
+}
+}  // namespace
+
+extern "C" {
+
 gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, const void* v, const float* g,
                          const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dv, float* dg,
                          float* dS0, void* ws, size_t ws_bytes, void* stream) {
@@ -1164,8 +1190,92 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
   r.H = dims->H;
   const StateView r0 = state_plain(const_cast<float*>(dS_T), hw);
 
-  // Segment states of both recurrences: their pass-1 walks share one launch.
+  // 2a. dv: queries k, outputs dv (a dv-half per slice); the final state is
+  //     the gradient leaving the first token (dS0 after its decay, below).
+  WalkArgs rv = r;
+  rv.Q = tok_view(k, 2, dims, DK, 0, true);
+  rv.O = tok_view(dv, osz, dims, DV, hw, true);
+  // 2b. dk: keys a dv-half of dO, values q (the state is the transpose),
+  //     queries the same half of v.
+  WalkArgs rk_ = r;
+  rk_.X = tok_view(dO, 2, dims, DV, hw, true);
+  rk_.Y = tok_view(q, 2, dims, DK, 0, true);
+  rk_.Q = tok_view(v, 2, dims, DV, hw, true);
+  rk_.O = tok_view(dk_part, 4, dims, DK, 0, true);
+
+  // dq and dk run as one walk per dv-half.  The first half writes fp32 sums;
+  // the second adds them to its own (a fixed order), writes the gradient and
+  // its dot product with q (k) for the log-decay gradient.
+  SegPlan sp1 = sp;
+  sp1.ns = 1;
+  auto half = [&](WalkArgs a, int hh) {
+    a.X = shifted(a.X, (int64_t)hh * hw, 2);
+    a.Q = shifted(a.Q, (int64_t)hh * hw, 2);
+    return a;
+  };
+  auto second_half = [&](WalkArgs a, const TokView& part, void* out, const void* dotted, float* rdot, bool backwards) {
+    a.acc = part;
+    a.O = tok_view(out, osz, dims, DK, 0, backwards);
+    a.D = tok_view(dotted, 2, dims, DK, 0, backwards);
+    a.rdot = token_floats(rdot, dims, backwards);
+    return a;
+  };
+  StateView rk0 = r0;                                  // dk's state is the transpose of dv's
+  rk0.sx = r0.sy;
+  rk0.sy = r0.sx;
   hipError_t e = hipSuccess;
+
+  if (sp.nseg == 2) {
+    // Two segments, staggered over three launches instead of a state pass
+    // and a scan: each walk's second segment starts from the state that its
+    // first segment (the same walk, or the dv walk of the same recurrence)
+    // left in the workspace one launch earlier, and the second dv-half of dq
+    // and dk follows its first half by one launch.
+    //   launch 0: dq, dk first half, segment 0; dv, segment 0
+    //   launch 1: dq, dk second half, segment 0; dq, dk first half, segment 1
+    //   launch 2: dq, dk second half, segment 1; dv, segment 1
+    // Every launch holds 4 B H walks of the same length.
+    StateView fmid = state_transposed((float*)(w + p.off_segf), hw);   // S entering segment 1
+    StateView rmid = state_plain((float*)(w + p.off_segr), hw);        // U entering segment 1 (reversed time)
+    StateView rkmid = rmid;
+    rkmid.sx = rmid.sy;
+    rkmid.sy = rmid.sx;
+    auto seg_walk = [&](WalkArgs a, const SegPlan& plan, int seg, StateView zinit, StateView zfin) {
+      a = segments_args(a, plan, zinit, zfin);
+      a.zfin_only_seg = -1;
+      a.nseg_launch = 1;
+      a.seg_offset = seg;
+      return a;
+    };
+    const TokView dq_acc = tok_view(dq_part, 4, dims, DK, 0, false);
+    const TokView dk_acc = tok_view(dk_part, 4, dims, DK, 0, true);
+    const int n1 = (int)BH, n2 = (int)(BH * sp.ns);
+    const bool bf = dims->out_dtype == GLA_BF16;
+    WalkArgs l0[4] = {seg_walk(half(f, 0), sp1, 0, f0, fmid), seg_walk(half(rk_, 0), sp1, 0, rk0, StateView{}),
+                      seg_walk(rv, sp, 0, r0, rmid), WalkArgs{}};
+    const int c0[4] = {n1, n1, n2, 0};
+    e = launch_out_walk_quad(l0, c0, bf ? QUAD_F32_BF16 : QUAD_F32_F32, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd walks, launch 0");
+    WalkArgs l1[4] = {seg_walk(second_half(half(f, 1), dq_acc, dq, q, rq, false), sp1, 0, shifted(f0, hw),
+                               shifted(fmid, hw)),
+                      seg_walk(second_half(half(rk_, 1), dk_acc, dk, k, rk, true), sp1, 0, shifted(rk0, hw),
+                               StateView{}),
+                      seg_walk(half(f, 0), sp1, 1, fmid, ffin), seg_walk(half(rk_, 0), sp1, 1, rkmid, StateView{})};
+    const int c1[4] = {n1, n1, n1, n1};
+    e = launch_out_walk_quad(l1, c1, bf ? QUAD_ACC_BF16_F32 : QUAD_ACC_F32_F32, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd walks, launch 1");
+    WalkArgs l2[4] = {seg_walk(second_half(half(f, 1), dq_acc, dq, q, rq, false), sp1, 1, shifted(fmid, hw),
+                               shifted(ffin, hw)),
+                      seg_walk(second_half(half(rk_, 1), dk_acc, dk, k, rk, true), sp1, 1, shifted(rkmid, hw),
+                               StateView{}),
+                      seg_walk(rv, sp, 1, rmid, state_plain(dS0, hw)), WalkArgs{}};
+    const int c2[4] = {n1, n1, n2, 0};
+    e = launch_out_walk_quad(l2, c2, bf ? QUAD_ACC_BF16_BF16 : QUAD_ACC_F32_F32, st);
+    if (e != hipSuccess) return device_err(e, "gla_chunk_bwd walks, launch 2");
+    return bwd_tail(dims, p, rq, rk, dg, dS_T, S_T, dS0, g, w, st);
+  }
+
+  // Segment states of both recurrences: their pass-1 walks share one launch.
   StateView fseg = f0, rseg = r0;
   if (sp.nseg > 1) {
     fseg = seg_view(seg_f, f0, sp.entries());
@@ -1180,66 +1290,21 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
     fseg = coarse(fseg, sp);
     rseg = coarse(rseg, sp);
   }
-  // 2a. dv: queries k, outputs dv (a dv-half per slice); the final state is
-  //     the gradient leaving the first token (dS0 after its decay, below).
-  WalkArgs rv = r;
-  rv.Q = tok_view(k, 2, dims, DK, 0, true);
-  rv.O = tok_view(dv, osz, dims, DV, hw, true);
-  // 2b. dk: keys a dv-half of dO, values q (the state is the transpose),
-  //     queries the same half of v.
-  WalkArgs rk_ = r;
-  rk_.X = tok_view(dO, 2, dims, DV, hw, true);
-  rk_.Y = tok_view(q, 2, dims, DK, 0, true);
-  rk_.Q = tok_view(v, 2, dims, DV, hw, true);
-  rk_.O = tok_view(dk_part, 4, dims, DK, 0, true);
   StateView rkseg = rseg;
   rkseg.sx = rseg.sy;
   rkseg.sy = rseg.sx;
-
-  // dq and dk run as one walk per dv-half.  The first half writes fp32 sums;
-  // the second adds them to its own (a fixed order), writes the gradient and
-  // its dot product with q (k) for the log-decay gradient.
-  SegPlan sp1 = sp;
-  sp1.ns = 1;
-  auto half = [&](WalkArgs a, int hh) {
-    a.X = shifted(a.X, (int64_t)hh * hw, 2);
-    a.Q = shifted(a.Q, (int64_t)hh * hw, 2);
-    return a;
-  };
   WalkArgs q0 = segments_args(half(f, 0), sp1, fseg, ffin);
   WalkArgs k0 = segments_args(half(rk_, 0), sp1, rkseg, StateView{});
-  WalkArgs q1 = segments_args(half(f, 1), sp1, shifted(fseg, hw), shifted(ffin, hw));
-  WalkArgs k1 = segments_args(half(rk_, 1), sp1, shifted(rkseg, hw), StateView{});
-  q1.acc = q0.O;
-  q1.O = tok_view(dq, osz, dims, DK, 0, false);
-  q1.D = tok_view(q, 2, dims, DK, 0, false);
-  q1.rdot = token_floats(rq, dims, false);
-  k1.acc = k0.O;
-  k1.O = tok_view(dk, osz, dims, DK, 0, true);
-  k1.D = tok_view(k, 2, dims, DK, 0, true);
-  k1.rdot = token_floats(rk, dims, true);
+  WalkArgs q1 = segments_args(second_half(half(f, 1), q0.O, dq, q, rq, false), sp1, shifted(fseg, hw),
+                              shifted(ffin, hw));
+  WalkArgs k1 = segments_args(second_half(half(rk_, 1), k0.O, dk, k, rk, true), sp1, shifted(rkseg, hw), StateView{});
   const int nw = (int)(BH * sp1.nseg);
   e = launch_out_walk_pair(q0, nw, k0, nw, 0, st);
   if (e == hipSuccess) e = launch_out_walk_pair(q1, nw, k1, nw, dims->out_dtype == GLA_BF16, st);
   if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dq/dk walks");
   e = walk_segments(rv, out_variant, sp, rseg, state_plain(dS0, hw), BH, st);
   if (e != hipSuccess) return device_err(e, "gla_chunk_bwd dv walk");
-
-  // 3. q.dq - k.dk and its in-chunk suffix sums
-  BwdFinishArgs fa{};
-  fa.rq = rq;
-  fa.rk = rk;
-  fa.dg = dg;
-  fa.chunk_r = (float*)(w + p.off_r);
-  fa.B = dims->B;
-  fa.T = dims->T;
-  fa.H = dims->H;
-  fa.n_chunks = sp.n_chunks;
-  e = launch_bwd_finish(fa, st);
-  if (e != hipSuccess) return device_err(e, "gla_chunk_bwd finish");
-  // 4. d-log-decay: add later chunks and <dS_T, S_T>; dS0 through the first decay
-  e = launch_dg_finish(dg, fa.chunk_r, dS_T, S_T, dS0, g, dims->B, dims->T, dims->H, sp.n_chunks, st);
-  return device_err(e, "gla_chunk_bwd dg finish");
+  return bwd_tail(dims, p, rq, rk, dg, dS_T, S_T, dS0, g, w, st);
 }
 
 }  // extern "C"

@@ -77,12 +77,24 @@ struct WalkArgs {
 };
 
 hipError_t launch_walk(const WalkArgs& a, int variant, int nwg, hipStream_t st);
-// Two independent bf16 state-only walks in one launch (nwg0 + nwg1
-// workgroups).
 // Two bf16 walks with output in one launch (nwg0 + nwg1 workgroups).
 hipError_t launch_out_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, int out_bf16,
                                 hipStream_t st);
+// Two independent bf16 state-only walks in one launch (nwg0 + nwg1
+// workgroups).
 hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st);
+// Up to four bf16 walks with output in one launch (nwg[i] workgroups each,
+// zero to skip one), in two groups of compile-time variants named by `kind`
+// (group A: walks 0 and 1, output type and partial sums; group B: walks 2 and
+// 3, output type, no partial sums).
+enum WalkQuadKind {
+  QUAD_F32_F32 = 0,        // A: float out;                B: float out
+  QUAD_F32_BF16 = 1,       // A: float out;                B: bf16 out
+  QUAD_ACC_F32_F32 = 2,    // A: float out, partial sums;  B: float out
+  QUAD_ACC_BF16_F32 = 3,   // A: bf16 out, partial sums;   B: float out
+  QUAD_ACC_BF16_BF16 = 4,  // A: bf16 out, partial sums;   B: bf16 out
+};
+hipError_t launch_out_walk_quad(const WalkArgs* a, const int* nwg, int kind, hipStream_t st);
 int walk_slices(int variant);
 // Z0 row of batch-head bh: z0_idx[bh / H] * H + bh % H when z0_idx is set.
 hipError_t launch_seg_scan(float* buf, const float* decay, const float* Z0, const int32_t* z0_idx, int H,

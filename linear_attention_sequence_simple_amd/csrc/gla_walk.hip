@@ -1240,6 +1240,56 @@ hipError_t launch_out_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1
   return hipGetLastError();
 }
 
+// Up to four bf16 walks with output in one launch, in two groups of two
+// compile-time variants: workgroups [o[i], o[i+1]) run a[i]; a[0], a[1] as
+// (TA, ACCA), a[2], a[3] as (TB, ACCB).  Walks with no workgroups are skipped.
+struct WalkQuad {
+  WalkArgs a[4];
+  int o[5];
+};
+
+template <class TA, bool ACCA, class TB, bool ACCB>
+__global__ void __launch_bounds__(WalkShape<WALK_FWD_OUT>::THREADS, 1) walk_out_quad_kernel(WalkQuad w) {
+  __shared__ WalkSmem<bf16, 3, true> sm;
+  const int x = (int)blockIdx.x;
+  const int i = (x >= w.o[1]) + (x >= w.o[2]) + (x >= w.o[3]);
+  const int local = x - w.o[i], nwg = w.o[i + 1] - w.o[i];
+  // the walk's arguments read in place from the kernel-argument segment (the
+  // parameter is its first and only explicit argument): indexing the
+  // parameter itself would copy all four argument sets to scratch memory
+  using KArgs = const __attribute__((address_space(4))) WalkQuad;
+  const WalkArgs& a = *(const WalkArgs*)&((KArgs*)__builtin_amdgcn_kernarg_segment_ptr())->a[i];
+  if (i < 2)
+    walk_block<bf16, TA, 3, WALK_FWD_OUT, false, false, ACCA>(a, sm, local, nwg);
+  else
+    walk_block<bf16, TB, 3, WALK_FWD_OUT, false, false, ACCB>(a, sm, local, nwg);
+}
+
+hipError_t launch_out_walk_quad(const WalkArgs* a, const int* nwg, int kind, hipStream_t st) {
+  WalkQuad w;
+  w.o[0] = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (nwg[i] < 0) return hipErrorInvalidValue;
+    w.a[i] = a[i];
+    w.o[i + 1] = w.o[i] + nwg[i];
+  }
+  // the walks of group A add partial sums exactly in the ACC kinds; group B never does
+  const bool acc_a = kind == QUAD_ACC_F32_F32 || kind == QUAD_ACC_BF16_F32 || kind == QUAD_ACC_BF16_BF16;
+  for (int i = 0; i < 4; ++i)
+    if (nwg[i] > 0 && (a[i].acc.p != nullptr) != (i < 2 && acc_a)) return hipErrorInvalidValue;
+  if (w.o[4] == 0) return hipSuccess;
+  const dim3 grid(w.o[4]), block(WalkShape<WALK_FWD_OUT>::THREADS);
+  switch (kind) {
+    case QUAD_F32_F32: hipLaunchKernelGGL((walk_out_quad_kernel<float, false, float, false>), grid, block, 0, st, w); break;
+    case QUAD_F32_BF16: hipLaunchKernelGGL((walk_out_quad_kernel<float, false, bf16, false>), grid, block, 0, st, w); break;
+    case QUAD_ACC_F32_F32: hipLaunchKernelGGL((walk_out_quad_kernel<float, true, float, false>), grid, block, 0, st, w); break;
+    case QUAD_ACC_BF16_F32: hipLaunchKernelGGL((walk_out_quad_kernel<bf16, true, float, false>), grid, block, 0, st, w); break;
+    case QUAD_ACC_BF16_BF16: hipLaunchKernelGGL((walk_out_quad_kernel<bf16, true, bf16, false>), grid, block, 0, st, w); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_state_walk_pair(const WalkArgs& a0, int nwg0, const WalkArgs& a1, int nwg1, hipStream_t st) {
   hipLaunchKernelGGL((walk_pair_kernel<bf16, 3>), dim3(nwg0 + nwg1), dim3(WalkShape<WALK_FWD_STATE>::THREADS), 0,
                      st, a0, a1, nwg0);

@@ -75,6 +75,29 @@ def test_segments(T, segments):
     check(d, got)
 
 
+@pytest.mark.parametrize("T,s0,dst,out", [(1100, True, True, "f32"), (1100, False, False, "bf16"),
+                                          (260, True, False, "f32"), (385, False, True, "bf16"),
+                                          (2048, True, True, "bf16")])
+def test_two_segments(T, s0, dst, out):
+    """Two segments: the walks' second segments start from the states their
+    first segments left one launch earlier (no state pass); segment 1 holds
+    one chunk at T = 260 and 385."""
+    d = inputs("bwd_bf16_b4_t4096", seed=40 + T, B=1, T=T, H=2, S0="normal0.1", with_dO=True, with_dS_T=True)
+    print(f"case bwd two segments T={T} S0={s0} dS_T={dst} out={out}", flush=True)
+    out_dtype = torch.bfloat16 if out == "bf16" else torch.float32
+    got = run_bwd(d, s0, dst, out_dtype=out_dtype, segments=2)
+    if out == "f32":
+        check(d, got, s0, dst)
+        return
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["dO"], d["S0"] if s0 else None,
+                          d["dS_T"] if dst else None)
+    for name, x, y in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close_bf16_out(x, y, TOL, name + "(bf16)")
+    assert_close(got[3], ref[3], TOL, "dg")
+    if s0 or dst:
+        assert_close(got[4], ref[4], TOL, "dS0")
+
+
 def test_bf16_gradients():
     # gradients written in bf16: elementwise bound of the rounding on top of
     # the tolerance; dg stays fp32
@@ -98,6 +121,20 @@ def test_backward_workload_sampled():
         assert_close(sub(x), y, TOL, name)
     for x in got[:4]:
         assert np.isfinite(x).all()
+
+
+def test_backward_workload_bf16_sampled():
+    """The timed backward: B=4, H=16, T=4096, bf16 gradients (two segments,
+    staggered launches); every gradient of sampled (b, h) against the oracle
+    with the elementwise bf16-output bound."""
+    d = inputs("bwd_bf16_b4_t4096", seed=1, with_dO=True)
+    got = run_bwd(d, S0=False, dS_T=False, out_dtype=torch.bfloat16)
+    bs, hs = [1, 2], [0, 15]
+    sub = lambda x: x[np.ix_(bs, range(x.shape[1]), hs)]
+    ref = oracle.backward(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]), sub(d["dO"]))
+    for name, x, y in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        assert_close_bf16_out(sub(x), y, TOL, name + "(bf16)")
+    assert_close(sub(got[3]), ref[3], TOL, "dg")
 
 
 def test_longest_supported_sequence():
