@@ -80,7 +80,9 @@ typedef enum { GLA_OP_FWD = 0, GLA_OP_BWD = 1, GLA_OP_FWD_VARLEN_Q16 = 2 } gla_o
  * pick its launch plan (the default; a zero-initialised struct gets it);
  * n > 0 splits every (batch, head) walk over the chunks into n segments of
  * whole chunks (at most one per chunk), whose entering states come from a
- * state-only pass and a scan over the segments.  Any plan computes the same
+ * state-only pass and a scan over the segments (the bf16 backward with two
+ * segments instead starts each second segment from the state its first one
+ * left, one launch later).  Any plan computes the same
  * recurrence; results differ only by rounding.  The workspace size depends
  * on it, so pass the same dims to gla_workspace_size.  Negative values are
  * INVALID_ARGUMENT. */
