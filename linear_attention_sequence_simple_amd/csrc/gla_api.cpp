@@ -1235,6 +1235,16 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
     //   launch 1: dq, dk second half, segment 0; dq, dk first half, segment 1
     //   launch 2: dq, dk second half, segment 1; dv, segment 1
     // Every launch holds 4 B H walks of the same length.
+    // Segment 0 is the shorter: the second-half walks of launch 2 (the
+    // slowest walks) then cover fewer chunks, the first-half walks running
+    // beside them more, which balances the launches (13 of 32 chunks at the
+    // training shape).
+    const int c0 = std::max(1, std::min(sp.n_chunks - 1, (sp.n_chunks * 13 + 16) / 32));
+    SegPlan s0 = sp, s1 = sp;
+    s0.cps = c0;
+    s1.cps = sp.n_chunks - c0;
+    SegPlan s0h = s0, s1h = s1;
+    s0h.ns = s1h.ns = 1;
     StateView fmid = state_transposed((float*)(w + p.off_segf), hw);   // S entering segment 1
     StateView rmid = state_plain((float*)(w + p.off_segr), hw);        // U entering segment 1 (reversed time)
     StateView rkmid = rmid;
@@ -1244,33 +1254,34 @@ gla_status gla_chunk_bwd(const gla_dims* dims, const void* q, const void* k, con
       a = segments_args(a, plan, zinit, zfin);
       a.zfin_only_seg = -1;
       a.nseg_launch = 1;
-      a.seg_offset = seg;
+      a.seg_offset = 0;
+      a.chunk0 = seg ? c0 : 0;
       return a;
     };
     const TokView dq_acc = tok_view(dq_part, 4, dims, DK, 0, false);
     const TokView dk_acc = tok_view(dk_part, 4, dims, DK, 0, true);
     const int n1 = (int)BH, n2 = (int)(BH * sp.ns);
     const bool bf = dims->out_dtype == GLA_BF16;
-    WalkArgs l0[4] = {seg_walk(half(f, 0), sp1, 0, f0, fmid), seg_walk(half(rk_, 0), sp1, 0, rk0, StateView{}),
-                      seg_walk(rv, sp, 0, r0, rmid), WalkArgs{}};
-    const int c0[4] = {n1, n1, n2, 0};
-    e = launch_out_walk_quad(l0, c0, bf ? QUAD_F32_BF16 : QUAD_F32_F32, st);
+    WalkArgs l0[4] = {seg_walk(half(f, 0), s0h, 0, f0, fmid), seg_walk(half(rk_, 0), s0h, 0, rk0, StateView{}),
+                      seg_walk(rv, s0, 0, r0, rmid), WalkArgs{}};
+    const int nw0[4] = {n1, n1, n2, 0};
+    e = launch_out_walk_quad(l0, nw0, bf ? QUAD_F32_BF16 : QUAD_F32_F32, st);
     if (e != hipSuccess) return device_err(e, "gla_chunk_bwd walks, launch 0");
-    WalkArgs l1[4] = {seg_walk(second_half(half(f, 1), dq_acc, dq, q, rq, false), sp1, 0, shifted(f0, hw),
+    WalkArgs l1[4] = {seg_walk(second_half(half(f, 1), dq_acc, dq, q, rq, false), s0h, 0, shifted(f0, hw),
                                shifted(fmid, hw)),
-                      seg_walk(second_half(half(rk_, 1), dk_acc, dk, k, rk, true), sp1, 0, shifted(rk0, hw),
+                      seg_walk(second_half(half(rk_, 1), dk_acc, dk, k, rk, true), s0h, 0, shifted(rk0, hw),
                                StateView{}),
-                      seg_walk(half(f, 0), sp1, 1, fmid, ffin), seg_walk(half(rk_, 0), sp1, 1, rkmid, StateView{})};
-    const int c1[4] = {n1, n1, n1, n1};
-    e = launch_out_walk_quad(l1, c1, bf ? QUAD_ACC_BF16_F32 : QUAD_ACC_F32_F32, st);
+                      seg_walk(half(f, 0), s1h, 1, fmid, ffin), seg_walk(half(rk_, 0), s1h, 1, rkmid, StateView{})};
+    const int nw1[4] = {n1, n1, n1, n1};
+    e = launch_out_walk_quad(l1, nw1, bf ? QUAD_ACC_BF16_F32 : QUAD_ACC_F32_F32, st);
     if (e != hipSuccess) return device_err(e, "gla_chunk_bwd walks, launch 1");
-    WalkArgs l2[4] = {seg_walk(second_half(half(f, 1), dq_acc, dq, q, rq, false), sp1, 1, shifted(fmid, hw),
+    WalkArgs l2[4] = {seg_walk(second_half(half(f, 1), dq_acc, dq, q, rq, false), s1h, 1, shifted(fmid, hw),
                                shifted(ffin, hw)),
-                      seg_walk(second_half(half(rk_, 1), dk_acc, dk, k, rk, true), sp1, 1, shifted(rkmid, hw),
+                      seg_walk(second_half(half(rk_, 1), dk_acc, dk, k, rk, true), s1h, 1, shifted(rkmid, hw),
                                StateView{}),
-                      seg_walk(rv, sp, 1, rmid, state_plain(dS0, hw)), WalkArgs{}};
-    const int c2[4] = {n1, n1, n2, 0};
-    e = launch_out_walk_quad(l2, c2, bf ? QUAD_ACC_BF16_BF16 : QUAD_ACC_F32_F32, st);
+                      seg_walk(rv, s1, 1, rmid, state_plain(dS0, hw)), WalkArgs{}};
+    const int nw2[4] = {n1, n1, n2, 0};
+    e = launch_out_walk_quad(l2, nw2, bf ? QUAD_ACC_BF16_BF16 : QUAD_ACC_F32_F32, st);
     if (e != hipSuccess) return device_err(e, "gla_chunk_bwd walks, launch 2");
     return bwd_tail(dims, p, rq, rk, dg, dS_T, S_T, dS0, g, w, st);
   }

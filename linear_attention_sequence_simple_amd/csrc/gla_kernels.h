@@ -64,6 +64,7 @@ struct WalkArgs {
   int64_t seg_decay_bh_stride;
   int64_t B, T;
   int H, n_chunks, cps, ns, nseg_launch, seg_offset;
+  int chunk0;           // segment s of the walk covers chunks chunk0 + s*cps onwards (cps of them)
   // Packed sequences (null: B sequences of T tokens): sequence b is tokens
   // [cu[b], cu[b+1]) of a token axis of cu_total rows, the batch strides are
   // zero, and T and n_chunks bound its length in tokens and chunks.  Offsets

@@ -234,7 +234,7 @@ __device__ __forceinline__ void walk_wave(const WalkArgs& a, WalkSmem<TIn, NC, M
   const float* gb = a.g + b * a.gsb + sq.t0 * a.gst + h * a.gsh;
 
   const int gseg = seg + a.seg_offset;
-  const int n_begin = gseg * a.cps;
+  const int n_begin = a.chunk0 + gseg * a.cps;
   const int n_end = min(sq.n_chunks, n_begin + a.cps);
   const int nloc = PACKED ? max(0, n_end - n_begin) : n_end - n_begin;   // packed: past a sequence's end, 0
 
@@ -660,7 +660,7 @@ __device__ __forceinline__ void prefill_wave(const WalkArgs& a, WalkSmem<bf16, 3
   const bf16* Qb = (const bf16*)a.Q.p + b * a.Q.sb + sq.t0 * a.Q.st + h * a.Q.sh + slice * a.Q.ss;
   const float* gb = a.g + b * a.gsb + sq.t0 * a.gst + h * a.gsh;
   const int gseg = seg + a.seg_offset;
-  const int n_begin = gseg * a.cps;
+  const int n_begin = a.chunk0 + gseg * a.cps;
   const int n_end = min(sq.n_chunks, n_begin + a.cps);
   const int nloc = PACKED ? max(0, n_end - n_begin) : n_end - n_begin;   // packed: past a sequence's end, 0
 
