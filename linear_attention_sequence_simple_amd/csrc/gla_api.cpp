@@ -142,6 +142,8 @@ gla_status check_dims(const gla_dims* d) {
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype))
     return fail(GLA_ERR_INVALID_ARGUMENT, "in_dtype/out_dtype must be GLA_F32 or GLA_BF16");
   if (d->B * d->H > (int64_t)1 << 24) return fail(GLA_ERR_UNSUPPORTED, "B*H too large");
+  // the walks address 32 token rows of a [B,T,H,dv] fp32 tensor with 32-bit offsets
+  if ((int64_t)d->H * DV * 4 * 32 >= (int64_t)1 << 31) return fail(GLA_ERR_UNSUPPORTED, "H too large");
   if ((d->T + CH - 1) / CH > (1 << 20)) return fail(GLA_ERR_UNSUPPORTED, "T too large");
   if (d->segments < 0) return fail(GLA_ERR_INVALID_ARGUMENT, "segments must be >= 0 (got %d)", d->segments);
   return GLA_OK;

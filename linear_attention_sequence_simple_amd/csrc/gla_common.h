@@ -245,16 +245,11 @@ __device__ __forceinline__ void regs_to_frag_split(const f32x16& t, int s, bf16x
 }
 
 __device__ __forceinline__ void store4_split(bf16* hi, bf16* lo, f32x4 v) {
-  bf16x4 h, l;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16 a, b;
-    split_bf16(v[e], a, b);
-    h[e] = a;
-    l[e] = b;
-  }
-  *(bf16x4*)hi = h;
-  *(bf16x4*)lo = l;
+  uint32_t h[2], l[2];
+  split_pk(v[0], v[1], h[0], l[0]);
+  split_pk(v[2], v[3], h[1], l[1]);
+  *(uint2*)hi = make_uint2(h[0], h[1]);
+  *(uint2*)lo = make_uint2(l[0], l[1]);
 }
 
 // The bf16 operand for sub-step s taken from result registers of a tile.

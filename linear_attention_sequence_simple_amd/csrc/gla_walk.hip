@@ -130,11 +130,29 @@ struct TileRegs {
   static constexpr int NP = CH * PPR;
   static constexpr int PER = (NP + NTHR - 1) / NTHR;
   uint4 r[PER];
+  // The pieces with index i of all threads cover rows (NTHR i)/PPR onwards, a
+  // group of at most GROWS rows.  Each load takes a workgroup-uniform address
+  // (the group's first row in memory order) and a 32-bit lane offset that is
+  // the same in every chunk, so no per-chunk 64-bit address arithmetic runs
+  // on the vector units; GROWS <= 32 keeps the offset within the 32-row bound
+  // the views guarantee.
+  static constexpr int group_rows() {
+    int m = 0;
+    for (int i = 0; i < PER; ++i) {
+      const int rows = (NTHR * i + NTHR - 1) / PPR - (NTHR * i) / PPR + 1;
+      m = rows > m ? rows : m;
+    }
+    return m;
+  }
+  static constexpr int GROWS = group_rows();
+  static_assert(GROWS <= 32, "a piece group must stay within 32 rows");
   __device__ __forceinline__ void load_piece(int i, const T* base, int64_t row_stride, int t0, int64_t T_len) {
     const int p = (threadIdx.x & (NTHR - 1)) + NTHR * i;
     const int row = p / PPR, cp = p % PPR;
-    r[i] = (p < NP && t0 + row < T_len) ? *(const uint4*)(base + (int64_t)(t0 + row) * row_stride + cp * EPP)
-                                        : make_uint4(0, 0, 0, 0);
+    const int g0 = (NTHR * i) / PPR;
+    const char* gb = tile_base(base, row_stride, (int64_t)t0 + g0, GROWS);
+    const uint32_t off = row_offset<T>(row - g0, cp * EPP, row_stride, GROWS);
+    r[i] = (p < NP && t0 + row < T_len) ? *(const uint4*)(gb + off) : make_uint4(0, 0, 0, 0);
   }
   __device__ __forceinline__ void load(const T* base, int64_t row_stride, int t0, int64_t T_len) {
 #pragma unroll

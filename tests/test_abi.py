@@ -94,7 +94,8 @@ def test_segments_plan_argument(L):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(T=0), 1), (dict(H=0), 1), (dict(dk=64), 2), (dict(dv=128), 2),
-    (dict(chunk=64), 2), (dict(in_dtype=5), 1), (dict(out_dtype=-1), 1), (dict(segments=-1), 1)])
+    (dict(chunk=64), 2), (dict(in_dtype=5), 1), (dict(out_dtype=-1), 1), (dict(segments=-1), 1),
+    (dict(B=1, H=1 << 17), 2)])
 def test_dims_validation(L, kw, status):
     st, _ = ws_size(L, gla.GLA_OP_FWD, dims(**kw))
     assert st == status
