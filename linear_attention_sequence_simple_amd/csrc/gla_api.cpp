@@ -152,11 +152,14 @@ gla_status check_dims(const gla_dims* d) {
 constexpr int64_t kStateElems = (int64_t)DK * DV;
 constexpr int kTargetWorkgroups = 256;   // one per compute unit
 
-// Segments per (batch, head, slice) walk: enough workgroups to cover the
-// chip, at least two chunks per segment; or the caller's count (dims->segments
-// > 0), at most one segment per chunk.
+// Segments per (batch, head, slice) walk: as many as the chip runs in one
+// round of workgroups (one per compute unit), at least two chunks per segment;
+// or the caller's count (dims->segments > 0), at most one segment per chunk.
+// A count that overflows the round leaves its last workgroups to walk their
+// whole segments on a nearly idle chip: 48 fp32 walks run 4 segments (192
+// workgroups) faster than 6 (288).
 int plan_segments(int64_t walkers, int n_chunks, int32_t forced) {
-  int nseg = (int)std::max<int64_t>(1, (kTargetWorkgroups + walkers - 1) / walkers);
+  int nseg = (int)std::max<int64_t>(1, kTargetWorkgroups / walkers);
   nseg = std::min(nseg, std::max(1, n_chunks / 2));
   if (forced > 0) nseg = std::min<int>(forced, n_chunks);
   return std::max(1, nseg);
