@@ -157,7 +157,8 @@ constexpr int kTargetWorkgroups = 256;   // one per compute unit
 // or the caller's count (dims->segments > 0), at most one segment per chunk.
 // A count that overflows the round leaves its last workgroups to walk their
 // whole segments on a nearly idle chip: 48 fp32 walks run 4 segments (192
-// workgroups) faster than 6 (288).
+// workgroups) faster than 6 (288), and a bf16 prefill of 5 x 16 heads runs
+// unsegmented (160 workgroups) in 0.70 of the time of 2 segments (320).
 int plan_segments(int64_t walkers, int n_chunks, int32_t forced) {
   int nseg = (int)std::max<int64_t>(1, kTargetWorkgroups / walkers);
   nseg = std::min(nseg, std::max(1, n_chunks / 2));
